@@ -1,0 +1,224 @@
+/*
+ * hkv.h — chunk store/retrieve for hybrid KDA+MLA model caches on MI355X.
+ *
+ * The library moves a hybrid model's cache between a paged GPU pool (the
+ * layout vLLM gives a model whose KDA linear-attention layers keep a
+ * recurrent state and whose MLA layers keep per-token latent KV) and
+ * contiguous chunk objects, one object per (chunk, object group):
+ *
+ *   store    : block-table gather, pool pages -> chunk objects;
+ *   retrieve : scatter of chunk objects into newly allocated block ids.
+ *
+ * Pages are opaque bytes: the KDA state (recurrent heads x d x d plus conv
+ * (conv_dim, kernel-1)) is one opaque page, as LMCache treats it ("Kimi-Linear"
+ * and "Kimi K3" recipes, introduction; "Hybrid Attention Models",
+ * Mamba / Linear-Attention Hybrids), so the copies are exact byte copies.
+ *
+ * Conventions for every call:
+ *   - returns hkv_status: HKV_OK (0) or a negative error code; nothing aborts
+ *     or throws; hkv_last_error() gives a message for the calling thread;
+ *   - all validation happens on the host, synchronously, before any work is
+ *     enqueued; a call that returns an error has enqueued nothing (except
+ *     HKV_E_HIP, which reports a failure of the HIP runtime itself);
+ *   - "HOST" arrays are read only during the call; "DEVICE" buffers must stay
+ *     allocated until the stream has passed the enqueued work;
+ *   - store/retrieve enqueue on the caller's stream and never synchronise it.
+ *
+ * Sizes are bytes unless stated; block ids are int32 in [0, num_blocks).
+ */
+#ifndef HKV_H
+#define HKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t hkv_status;
+
+#define HKV_OK 0
+#define HKV_E_ARG (-1)       /* malformed argument (NULL, negative count, bad enum) */
+#define HKV_E_COVER (-2)     /* given N is not a multiple of 16 tokens or its MLA page
+                                does not cover the KDA state page */
+#define HKV_E_CHUNK (-3)     /* strict mode and the chunk minimum is not a multiple of N */
+#define HKV_E_BATCH (-4)     /* max_num_batched_tokens outside the allowed range */
+#define HKV_E_POOL (-5)      /* the pool holds no whole block (or more than INT32_MAX) */
+#define HKV_E_RANGE (-6)     /* a block id outside [0, num_blocks) */
+#define HKV_E_ALIAS (-7)     /* a retrieve target id repeated in one call, or two buffers
+                                of one call overlap */
+#define HKV_E_ALIGN (-8)     /* pool, object or workspace pointer not 16-byte aligned */
+#define HKV_E_WORKSPACE (-9) /* workspace NULL or smaller than hkv_workspace_size() */
+#define HKV_E_HIP (-10)      /* the HIP runtime reported an error (see hkv_last_error) */
+
+/* One rank's model shapes.  KDA state shapes are PER RANK: heads and conv_dim
+ * are already divided by the TP degree, because the KDA state is sharded
+ * across TP ranks while the MLA cache is replicated ("Kimi-Linear" recipe,
+ * Note; vLLM hybrid KV-cache blog, section 2.1 gives the two state shapes). */
+typedef struct hkv_model {
+  int32_t n_layers;        /* number of decoder layers, >= 1 */
+  const uint8_t* is_mla;   /* HOST [n_layers], model order: 1 = MLA layer, 0 = KDA layer */
+  int32_t kda_heads;       /* recurrent state heads per rank */
+  int32_t kda_head_dim;    /* d: the recurrent state is heads x d x d */
+  int32_t kda_state_bytes; /* bytes per recurrent-state element (4 = fp32) */
+  int32_t conv_dim;        /* conv state rows per rank */
+  int32_t conv_kernel;     /* conv kernel size; the state keeps kernel-1 columns */
+  int32_t conv_bytes;      /* bytes per conv-state element (2 = bf16) */
+  int32_t mla_width;       /* values per token per MLA layer (kv_lora_rank + rope dim, 576) */
+  int32_t mla_bytes;       /* bytes per MLA value (2 = bf16, 1 = fp8 e4m3) */
+} hkv_model;
+
+/* Unified block size N: the smallest multiple of 16 tokens whose MLA page
+ * (N x mla_width x mla_bytes) is at least one rank's KDA state page
+ * (heads x d x d x state_bytes + conv_dim x (conv_kernel-1) x conv_bytes).
+ * Defined in "Hybrid Attention Models", Mamba / Linear-Attention Hybrids,
+ * Step 1 (vLLM forces one block size across groups so the attention page
+ * covers the state page) and the "Kimi-Linear" recipe, Note (N follows the
+ * per-rank state).  A model without KDA layers gets N = 16.
+ * align_tokens must be 16 (the only step this library supports; 0 = 16).
+ * Errors: HKV_E_ARG (NULL pointers, non-positive shapes, align != 16). */
+hkv_status hkv_unified_block_size(const hkv_model* model, int32_t align_tokens,
+                                  int64_t* n_out);
+
+/* Everything a layout needs. */
+typedef struct hkv_layout_desc {
+  hkv_model model;
+  int64_t block_size;         /* N in tokens; 0 = derive with the rule above; nonzero
+                                 must be a multiple of 16 covering the KDA page
+                                 (else HKV_E_COVER) */
+  int64_t chunk_min_tokens;   /* >= 1: the chunk size is the smallest multiple of N at or
+                                 above it ("Kimi K3" recipe, Why these settings) */
+  int32_t strict_chunk_multiple; /* 1: HKV_E_CHUNK unless chunk_min_tokens % N == 0 (the
+                                 older rule, "Kimi-Linear" recipe, Why these settings) */
+  int32_t path;               /* 0 = path A, shared tensors with the unified padded page
+                                 (vLLM hybrid KV-cache blog, section 3.1);
+                                 1 = path B, packed per-layer offset + block stride
+                                 (same blog, section 3.2) */
+  int32_t separate_object_groups; /* 1: KDA and MLA layers go to different objects;
+                                 0: one object holds every layer ("Hybrid Attention
+                                 Models", Object-group separation) */
+  const int32_t* kv_group_of_layer; /* HOST [n_layers] KV-cache group of each layer, ids
+                                 0..G-1 all used; NULL = default: the MLA layers form one
+                                 group, the KDA layers in model order form
+                                 ceil(n_kda/n_mla) contiguous groups of sizes differing
+                                 by at most one, larger first (Mooncake K3 blog, "Flat
+                                 KV"); KDA groups are numbered before the MLA group */
+  uint64_t pool_bytes;        /* bytes of the pool the layout may use */
+  int64_t max_num_batched_tokens; /* 0 = skip; else must be >= N, and < 2N unless
+                                 object groups are separated (HKV_E_BATCH) ("Kimi-Linear"
+                                 recipe, Why these settings; "Hybrid Attention Models",
+                                 Step 2) */
+  uint64_t tile_bytes;        /* 0 = default; else the largest span one workgroup copies
+                                 (a multiple of 4096); a tuning knob, no effect on
+                                 results */
+} hkv_layout_desc;
+
+typedef struct hkv_layout hkv_layout; /* opaque; immutable after init; may be shared by
+                                         threads */
+
+/* Plans a layout.  Path A: every layer uses the unified page P = the largest
+ * real page (the MLA page), smaller KDA pages are padded to it; slab s holds
+ * the s-th layer of every KV group, pool_offset = s x num_blocks x P,
+ * stride P, num_blocks = pool_bytes / (slabs x P).  Path B: inside a group
+ * the layers' real pages are packed in model order (running offset), the
+ * block stride is the largest group total, num_blocks = pool_bytes /
+ * stride.  Object layout: layer-major in model order, then the k blocks of
+ * the chunk, real page bytes only, no header; for MLA layers this is an
+ * [L_obj][chunk_tokens][mla_width] array.
+ * Errors: HKV_E_ARG, HKV_E_COVER, HKV_E_CHUNK, HKV_E_BATCH, HKV_E_POOL.
+ * On success *out owns heap memory released by hkv_layout_destroy. */
+hkv_status hkv_layout_init(const hkv_layout_desc* desc, hkv_layout** out);
+
+/* Releases a layout.  NULL is ignored.  The caller must not destroy a
+ * layout while a call that uses it is running on another thread. */
+void hkv_layout_destroy(hkv_layout* layout);
+
+typedef struct hkv_layout_info {
+  int64_t block_size;        /* N (tokens) */
+  int64_t chunk_tokens;      /* C (tokens), a multiple of N */
+  int32_t blocks_per_chunk;  /* k = C / N */
+  int32_t n_layers;
+  int32_t n_kv_groups;       /* G */
+  int32_t n_obj_groups;      /* O: 1 or 2 */
+  int64_t num_blocks;        /* valid block ids are [0, num_blocks) */
+  int32_t path;              /* 0 = A, 1 = B */
+  int32_t n_slabs;           /* path A: tensors = largest group size; path B: 0 */
+  uint64_t unified_page_bytes; /* path A: P; path B: 0 */
+  uint64_t block_stride;     /* bytes between consecutive block ids of one layer */
+  uint64_t pool_bytes_used;  /* bytes of the pool the layout addresses */
+  uint64_t obj_bytes[2];     /* bytes of one chunk's object of each object group (0 if
+                                unused) */
+  uint64_t chunk_payload_bytes; /* obj_bytes[0] + obj_bytes[1]: bytes moved per chunk */
+} hkv_layout_info;
+
+/* Copies the layout's summary.  Errors: HKV_E_ARG. */
+hkv_status hkv_layout_info_get(const hkv_layout* layout, hkv_layout_info* out);
+
+typedef struct hkv_layer_info {
+  int32_t is_mla;
+  int32_t kv_group;          /* index into the block table's group axis */
+  int32_t obj_group;         /* which object of the chunk holds this layer */
+  int32_t slot;              /* position inside its KV group (path A: its slab) */
+  uint64_t page_bytes;       /* real bytes of one page (copied) */
+  uint64_t reserved_bytes;   /* bytes reserved per block (path A: P, padding included) */
+  uint64_t pool_offset;      /* byte offset of block 0's page in the pool */
+  uint64_t stride;           /* bytes between the pages of consecutive block ids */
+  uint64_t obj_offset;       /* byte offset of block j=0's page inside its object; block j
+                                sits at obj_offset + j * page_bytes */
+} hkv_layer_info;
+
+/* Copies one layer's placement.  Errors: HKV_E_ARG (bad layer index). */
+hkv_status hkv_layer_info_get(const hkv_layout* layout, int32_t layer, hkv_layer_info* out);
+
+/* One call's chunks. */
+typedef struct hkv_chunk_batch {
+  int32_t n_chunks;          /* >= 0; 0 is a no-op */
+  const int32_t* block_ids;  /* HOST [n_chunks][G][k]: chunk c's block ids in each KV
+                                group (one block table per group, vLLM hybrid KV-cache
+                                blog, section 2.2) */
+  void* const* objects;      /* HOST [n_chunks][O] DEVICE pointers, each to obj_bytes[o]
+                                bytes, 16-byte aligned, pairwise disjoint and disjoint
+                                from the pool */
+} hkv_chunk_batch;
+
+/* Device workspace bytes needed by a call with up to max_chunks chunks.
+ * Errors: HKV_E_ARG. */
+hkv_status hkv_workspace_size(const hkv_layout* layout, int32_t max_chunks, size_t* bytes);
+
+/* Store (gather): for every chunk c, layer l and block j < k, copies the
+ * page_bytes(l) bytes at pool + pool_offset(l) + block_ids[c][g(l)][j] x
+ * stride(l) to objects[c][o(l)] + obj_offset(l) + j x page_bytes(l).
+ * Padding and group slack are never read.  The pool is not modified.
+ * pool: DEVICE, 16-byte aligned, pool_bytes_used long.  workspace: DEVICE,
+ * 16-byte aligned, ws_bytes >= hkv_workspace_size(n_chunks); it is
+ * overwritten and must not be used by another call until the stream passes
+ * this one.  stream: a hipStream_t (NULL = the default stream).
+ * Repeated source ids are allowed.
+ * Errors: HKV_E_ARG, HKV_E_RANGE, HKV_E_ALIAS (objects overlap each other or
+ * the pool), HKV_E_ALIGN, HKV_E_WORKSPACE, HKV_E_HIP. */
+hkv_status hkv_store_chunks(const hkv_layout* layout, const void* pool,
+                            const hkv_chunk_batch* batch, void* workspace, size_t ws_bytes,
+                            void* stream);
+
+/* Retrieve (scatter): the inverse copy, objects -> pages of the given,
+ * newly allocated block ids.  Writes exactly the real page bytes of the
+ * addressed pages and nothing else (KDA padding, group slack and every other
+ * block are left as they were).  Because all groups share one block-id
+ * space, every id of the call must be distinct (HKV_E_ALIAS otherwise).
+ * Same buffer rules as hkv_store_chunks; objects are not modified.
+ * Errors: HKV_E_ARG, HKV_E_RANGE, HKV_E_ALIAS, HKV_E_ALIGN, HKV_E_WORKSPACE,
+ * HKV_E_HIP. */
+hkv_status hkv_retrieve_chunks(const hkv_layout* layout, void* pool,
+                               const hkv_chunk_batch* batch, void* workspace,
+                               size_t ws_bytes, void* stream);
+
+/* Message for the calling thread's last non-OK status ("" if none).  The
+ * pointer stays valid until the thread's next hkv_* call. */
+const char* hkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HKV_H */

@@ -1,0 +1,428 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Closed forms the pages print (N = 944 / 1888, chunk negotiation, budget
+rules, K3 grouping), structural properties of both pool layouts, a second
+formulation of store through strided views, round-trip identity, exact
+written-byte counts, and brute force over every injective id assignment on
+tiny pools.
+"""
+import itertools
+
+import numpy as np
+import pytest
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+import oracle
+import workloads
+from tests import golden_io
+from tests.invariants import (check_live_pages_disjoint, check_objects, check_path_a,
+                              check_path_b, objects_by_views, payload_bytes)
+
+E = {"E_CHUNK": oracle.E_CHUNK, "E_BATCH": oracle.E_BATCH, "E_COVER": oracle.E_COVER}
+
+
+# ---------------------------------------------------------------- N rule
+@pytest.mark.parametrize("row", golden_io.rows("block_sizes.txt"), ids=lambda r: r[0][0])
+def test_unified_block_size_matches_pages(row):
+    vals, cite = row
+    heads, d, sb, conv, kern, cb, width, mb, n_expected = map(int, vals[1:])
+    kda = oracle.kda_page_bytes(heads, d, sb, conv, kern, cb)
+    n = oracle.unified_block_size(kda, width * mb, 16)
+    assert n == n_expected, cite
+    # minimality: 16 tokens fewer would not cover the state page
+    assert (n - 16) * width * mb < kda <= n * width * mb
+
+
+def test_state_dtype_reading_is_the_only_one_matching_both_pages():
+    """fp32 recurrent + bf16 conv is the only byte-width pair (of 1/2/4 B) for
+    which both 944 (TP=2) and 1888 (TP=1) come out ("Kimi-Linear" recipe,
+    Note); this pins the composition of the opaque page."""
+    hits = []
+    for sb in (1, 2, 4):
+        for cb in (1, 2, 4):
+            n2 = oracle.unified_block_size(oracle.kda_page_bytes(16, 128, sb, 6144, 4, cb), 1152)
+            n1 = oracle.unified_block_size(oracle.kda_page_bytes(32, 128, sb, 12288, 4, cb), 1152)
+            if (n2, n1) == (944, 1888):
+                hits.append((sb, cb))
+    assert hits == [(4, 2)]
+
+
+def test_alignment_reading_16_fits_the_printed_values():
+    """944 and 1888 admit steps of 4, 8 or 16 tokens, not 32 or 2; 16 is the
+    reading (a 32-token step gives 960, a 2-token step 1886)."""
+    kda2 = oracle.kda_page_bytes(16, 128, 4, 6144, 4, 2)
+    kda1 = oracle.kda_page_bytes(32, 128, 4, 12288, 4, 2)
+    ok = [a for a in (2, 4, 8, 16, 32, 64)
+          if oracle.unified_block_size(kda2, 1152, a) == 944
+          and oracle.unified_block_size(kda1, 1152, a) == 1888]
+    assert ok == [4, 8, 16]
+
+
+def test_tiny_block_size_and_tp_scaling():
+    # tiny: 2 x 16 x 16 fp32 + (96, 3) bf16 = 2624 B; 16 x 1152 = 18432 covers it
+    assert oracle.kda_page_bytes(2, 16, 4, 96, 4, 2) == 2 * 16 * 16 * 4 + 96 * 3 * 2
+    assert oracle.unified_block_size(2624, 1152) == 16
+    # N grows with the per-rank state: halving the state never raises N
+    for heads in (8, 16, 32, 64):
+        a = oracle.unified_block_size(oracle.kda_page_bytes(heads, 128, 4, 384 * heads, 4, 2), 1152)
+        b = oracle.unified_block_size(
+            oracle.kda_page_bytes(heads // 2, 128, 4, 192 * heads, 4, 2), 1152)
+        assert b <= a
+
+
+def test_block_size_cover_is_inclusive():
+    """An attention page only has to be at least as large as the state page
+    ("Hybrid Attention Models", Step 1): a state page of exactly 16 or 32
+    tokens' bytes gives that N, one byte more gives the next step."""
+    assert oracle.unified_block_size(16 * 1152, 1152) == 16
+    assert oracle.unified_block_size(16 * 1152 + 1, 1152) == 32
+    assert oracle.unified_block_size(32 * 576, 576) == 32
+    assert oracle.unified_block_size(0, 576) == 16
+    assert oracle.unified_block_size(1, 576) == 16
+
+
+def test_k3_given_block_size_is_accepted_and_covers():
+    """K3 at TP 8 runs with N = 768 ("Kimi K3" recipe, vLLM section); the
+    synthetic K3 rank shapes (6 x 128 x 128 fp32 + (2304, 3) bf16, fp8 MLA)
+    are covered by 768 tokens, and the layout takes the given N."""
+    cfg = workloads.make_config("k3_tp8")
+    lay = oracle.Layout(cfg.desc)
+    assert lay.summary["block_size"] == 768
+    assert lay.summary["chunk_tokens"] == 1536 and lay.summary["blocks_per_chunk"] == 2
+    kda = oracle.kda_page_bytes(6, 128, 4, 2304, 4, 2)
+    assert 768 * 576 >= kda
+
+
+def test_given_block_size_is_checked():
+    d = dict(workloads.make_config("kl_tp2").desc)
+    d["block_size"] = 928  # multiple of 16 but 928 x 1152 < 1,085,440
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.Layout(d)
+    assert e.value.status == oracle.E_COVER
+    d["block_size"] = 950  # covers but not a multiple of 16
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.Layout(d)
+    assert e.value.status == oracle.E_COVER
+
+
+# ---------------------------------------------------------------- chunk rule
+@pytest.mark.parametrize("row", golden_io.rows("chunk_negotiation.txt"),
+                         ids=lambda r: "-".join(r[0][:3]))
+def test_chunk_negotiation(row):
+    vals, cite = row
+    n, cmin, strict = int(vals[0]), int(vals[1]), int(vals[2])
+    if vals[3].startswith("E_"):
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.chunk_tokens(n, cmin, bool(strict))
+        assert e.value.status == E[vals[3]], cite
+    else:
+        assert oracle.chunk_tokens(n, cmin, bool(strict)) == int(vals[3]), cite
+
+
+def test_chunk_is_smallest_multiple():
+    for n in (16, 48, 768, 944):
+        for cmin in list(range(1, 3 * n + 2, max(1, n // 7))) + [n, 2 * n, 2 * n + 1]:
+            c = oracle.chunk_tokens(n, cmin)
+            assert c % n == 0 and c >= cmin and c - n < cmin
+
+
+# ---------------------------------------------------------------- budget rule
+@pytest.mark.parametrize("row", golden_io.rows("batch_budget.txt"),
+                         ids=lambda r: "-".join(r[0][:3]))
+def test_batch_budget(row):
+    vals, cite = row
+    n, budget, sep = int(vals[0]), int(vals[1]), int(vals[2])
+    # a model whose rule-N is below the given N so the given N is accepted
+    desc = workloads._desc([0, 1], 1, 4, 4, 1, 0, 1 << 26, block_size=n, chunk_min=n,
+                           separate=sep, max_batched=budget)
+    if vals[3] == "ok":
+        assert oracle.Layout(desc).summary["block_size"] == n, cite
+    else:
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.Layout(desc)
+        assert e.value.status == E[vals[3]], cite
+
+
+# ---------------------------------------------------------------- grouping
+def test_k3_groups_and_slabs_match_flat_kv():
+    g = golden_io.keyvals("k3_flat_kv_groups.txt")
+    is_mla = workloads.K3_93
+    assert len(is_mla) == g["n_layers"][0]
+    assert is_mla.count(0) == g["n_kda"][0] and is_mla.count(1) == g["n_mla"][0]
+    lay = oracle.Layout(workloads.make_config("k3_tp8").desc)
+    sizes = {}
+    for L in lay.layers:
+        sizes.setdefault((L["is_mla"], L["kv_group"]), 0)
+        sizes[(L["is_mla"], L["kv_group"])] += 1
+    kda = [v for (m, _), v in sorted(sizes.items()) if m == 0]
+    mla = [v for (m, _), v in sorted(sizes.items()) if m == 1]
+    assert kda == g["kda_group_sizes"] and mla == g["mla_group_size"]
+    assert lay.summary["n_slabs"] == g["slabs"][0]
+
+
+def test_groups_hold_one_layer_type_and_are_contiguous():
+    """Layers with equal specs share a group (vLLM hybrid KV-cache blog,
+    section 2.2): the default grouping never mixes KDA and MLA layers; KDA
+    groups are runs of consecutive KDA layers with sizes differing by <= 1."""
+    for name in workloads.CONFIG_NAMES:
+        lay = oracle.Layout(workloads.make_config(name).desc)
+        by_g = {}
+        for l, L in enumerate(lay.layers):
+            by_g.setdefault(L["kv_group"], []).append(l)
+        kda_sizes = []
+        kda_order = [l for l, L in enumerate(lay.layers) if not L["is_mla"]]
+        for g, members in sorted(by_g.items()):
+            kinds = {lay.layers[l]["is_mla"] for l in members}
+            assert len(kinds) == 1
+            if kinds == {0}:
+                idx = [kda_order.index(l) for l in members]
+                assert idx == list(range(idx[0], idx[0] + len(idx)))
+                kda_sizes.append(len(members))
+        assert max(kda_sizes) - min(kda_sizes) <= 1
+        assert kda_sizes == sorted(kda_sizes, reverse=True)
+        # groups numbered KDA first, MLA last
+        assert lay.layers[[l for l, L in enumerate(lay.layers) if L["is_mla"]][0]]["kv_group"] \
+            == lay.G - 1
+
+
+# ---------------------------------------------------------------- layouts
+@pytest.mark.parametrize("name", workloads.CONFIG_NAMES)
+def test_config_layouts_structure(name):
+    cfg = workloads.make_config(name)
+    lay = oracle.Layout(cfg.desc)
+    s = lay.summary
+    if s["path"] == 0:
+        check_path_a(s, lay.layers, cfg.desc["pool_bytes"])
+    else:
+        check_path_b(s, lay.layers, cfg.desc["pool_bytes"])
+    check_objects(s, lay.layers)
+
+
+def test_config_closed_forms():
+    """Values that follow from the shapes by hand arithmetic."""
+    s = oracle.Layout(workloads.make_config("kl_tp2").desc).summary
+    assert (s["block_size"], s["unified_page_bytes"], s["n_slabs"], s["num_blocks"]) == \
+        (944, 944 * 1152, 7, (16 << 30) // (7 * 944 * 1152))
+    s = oracle.Layout(workloads.make_config("kl_tp1").desc).summary
+    kda = 32 * 128 * 128 * 4 + 12288 * 3 * 2
+    mla = 1888 * 1152
+    assert s["block_stride"] == max(7 * kda, 7 * mla, 6 * kda) == 15_224_832
+    assert s["num_blocks"] == (64 << 30) // 15_224_832 == 4513
+    assert s["obj_bytes0"] == 20 * kda and s["obj_bytes1"] == 7 * mla
+    s = oracle.Layout(workloads.make_config("long_ctx").desc).summary
+    assert s["num_blocks"] == (100 << 30) // 15_224_832 == 7052
+    s = oracle.Layout(workloads.make_config("k3_tp8").desc).summary
+    assert (s["unified_page_bytes"], s["n_slabs"], s["num_blocks"]) == \
+        (768 * 576, 24, (24 << 30) // (24 * 768 * 576))
+    assert s["obj_bytes0"] == 2 * 69 * (6 * 128 * 128 * 4 + 2304 * 3 * 2)
+    assert s["obj_bytes1"] == 2 * 24 * 768 * 576
+    s = oracle.Layout(workloads.make_config("tiny").desc).summary
+    assert (s["block_size"], s["num_blocks"], s["n_kv_groups"], s["n_slabs"]) == (16, 64, 4, 1)
+
+
+# ---------------------------------------------------------------- small random layouts
+def small_desc(is_mla, path, sep, grouping, chunk_min, pool_blocks, conv_dim=4, mla_bytes=1):
+    """A layout with small pages (a 1 x 4 x 4 fp32 state plus a (conv_dim, 3)
+    bf16 conv state; 8 one-byte MLA values per token).  pool_blocks is how
+    many blocks of the largest possible per-block footprint fit."""
+    n_layers = len(is_mla)
+    if grouping == "default":
+        kvg = None
+    elif grouping == "by_type":
+        kvg = [int(m) for m in is_mla] if (0 in is_mla and 1 in is_mla) else [0] * n_layers
+    elif grouping == "one":
+        kvg = [0] * n_layers
+    else:  # each layer its own group
+        kvg = list(range(n_layers))
+    d = workloads._desc(is_mla, 1, 4, conv_dim, mla_bytes, path, 1, chunk_min=chunk_min,
+                        kv_group_of_layer=kvg, separate=sep, mla_width=8)
+    # the worst-case per-block footprint is bounded by n_layers x the largest page
+    lay_probe = oracle.Layout(dict(d, pool_bytes=1 << 30))
+    page_max = max(L["reserved_bytes"] for L in lay_probe.layers)
+    d["pool_bytes"] = pool_blocks * n_layers * page_max + 7
+    return d
+
+
+layout_params = st.tuples(
+    st.lists(st.integers(0, 1), min_size=1, max_size=7),     # is_mla
+    st.integers(0, 1),                                        # path
+    st.integers(0, 1),                                        # separate object groups
+    st.sampled_from(["default", "by_type", "one", "each"]),  # grouping
+    st.integers(1, 40),                                       # chunk minimum (tokens)
+    st.integers(1, 5),                                        # pool size factor
+    st.sampled_from([4, 5, 8]),                               # conv_dim (5: page not 16-B)
+)
+
+
+@settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(layout_params, st.integers(0, 2**31 - 1))
+def test_random_layouts_store_retrieve_properties(params, seed):
+    is_mla, path, sep, grouping, cmin, pf, conv = params
+    d = small_desc(is_mla, path, sep, grouping, cmin, pf, conv_dim=conv)
+    lay = oracle.Layout(d)
+    s = lay.summary
+    (check_path_a if path == 0 else check_path_b)(s, lay.layers, d["pool_bytes"])
+    check_objects(s, lay.layers)
+    check_live_pages_disjoint(s, lay.layers)
+
+    rng = np.random.default_rng(seed)
+    per_chunk = lay.G * lay.k
+    max_chunks = s["num_blocks"] // per_chunk
+    if max_chunks == 0:
+        return
+    n = int(rng.integers(1, max_chunks + 1))
+    used = s["pool_bytes_used"]
+    pool0 = rng.integers(0, 256, used, dtype=np.uint8)
+    ids = rng.permutation(s["num_blocks"])[:n * per_chunk].astype(np.int32)
+    ids = ids.reshape(n, lay.G, lay.k)
+    objs = [[np.zeros(lay.obj_bytes(o), np.uint8) for o in range(lay.O)] for _ in range(n)]
+    pool_copy = pool0.copy()
+    lay.store(pool0, ids, objs)
+    # I1: store leaves the pool unchanged
+    assert np.array_equal(pool0, pool_copy)
+    # I2: a second formulation (gathered rows of strided views) agrees
+    ref = objects_by_views(s, lay.layers, pool0, ids)
+    for c in range(n):
+        for o in range(lay.O):
+            assert np.array_equal(objs[c][o], ref[c][o])
+    # retrieve into fresh ids, on three backgrounds
+    fresh = rng.permutation(s["num_blocks"])[:n * per_chunk].astype(np.int32)
+    fresh = fresh.reshape(n, lay.G, lay.k)
+    objs_copy = [[a.copy() for a in row] for row in objs]
+    r_lo = np.zeros(used, np.uint8)
+    r_hi = np.full(used, 0xFF, np.uint8)
+    r_rand = rng.integers(0, 256, used, dtype=np.uint8)
+    r_rand0 = r_rand.copy()
+    for buf in (r_lo, r_hi, r_rand):
+        lay.retrieve(buf, fresh, objs)
+    # I5: retrieve leaves the objects unchanged
+    for c in range(n):
+        for o in range(lay.O):
+            assert np.array_equal(objs[c][o], objs_copy[c][o])
+    # I4: exactly the real page bytes are written (padding and slack are not)
+    written = (r_lo != 0) | (r_hi != 0xFF)
+    assert int(written.sum()) == payload_bytes(s, n)
+    assert np.array_equal(r_lo[written], r_hi[written])
+    assert np.array_equal(r_rand[~written], r_rand0[~written])
+    assert np.array_equal(r_rand[written], r_lo[written])
+    # I3: round trip: storing the retrieved ids reproduces the objects
+    objs2 = [[np.zeros(lay.obj_bytes(o), np.uint8) for o in range(lay.O)] for _ in range(n)]
+    lay.store(r_rand, fresh, objs2)
+    for c in range(n):
+        for o in range(lay.O):
+            assert np.array_equal(objs2[c][o], objs[c][o])
+
+
+def test_mla_object_is_chunk_tokens_by_latent_array():
+    """MLA pages are (block_size, 576) rows of a (num_blocks, block_size, 576)
+    view (vLLM hybrid KV-cache blog, section 4.2); the MLA object of a chunk
+    is then the [L_mla, chunk_tokens, 576] array of its k blocks."""
+    desc = workloads._desc([0, 1, 0, 1, 1], 1, 4, 4, 2, 0, 1 << 22, chunk_min=40, mla_width=8)
+    lay = oracle.Layout(desc)
+    s = lay.summary
+    N, C, k = s["block_size"], s["chunk_tokens"], s["blocks_per_chunk"]
+    assert k == 3 and C == 3 * N
+    rng = np.random.default_rng(7)
+    pool = rng.integers(0, 256, s["pool_bytes_used"], dtype=np.uint8)
+    ids = rng.permutation(s["num_blocks"])[:2 * lay.G * k].astype(np.int32).reshape(2, lay.G, k)
+    objs = [[np.zeros(lay.obj_bytes(o), np.uint8) for o in range(lay.O)] for _ in range(2)]
+    lay.store(pool, ids, objs)
+    mla_layers = [l for l, L in enumerate(lay.layers) if L["is_mla"]]
+    width = 8 * 2
+    for c in range(2):
+        obj = objs[c][1].reshape(len(mla_layers), C, width)
+        for i, l in enumerate(mla_layers):
+            L = lay.layers[l]
+            # the layer's (num_blocks, N, width) view inside its slab
+            v = pool[L["pool_offset"]:L["pool_offset"] + s["num_blocks"] * L["stride"]]
+            v = v.reshape(s["num_blocks"], L["stride"])[:, :N * width].reshape(-1, N, width)
+            tokens = np.concatenate([v[b] for b in ids[c, L["kv_group"]]], axis=0)
+            assert np.array_equal(obj[i], tokens)
+
+
+# ---------------------------------------------------------------- brute force
+BRUTE = [
+    # (is_mla, path, sep, grouping, chunk_min, n_chunks, pool_factor)
+    ([0, 0, 0, 1], 0, 1, "default", 1, 1, 1),
+    ([0, 0, 0, 1], 1, 1, "default", 1, 1, 1),
+    ([0, 1, 0, 1], 0, 0, "by_type", 1, 2, 1),
+    ([0, 1, 0, 1], 1, 1, "by_type", 17, 1, 1),
+    ([0, 0, 1], 1, 1, "one", 20, 2, 1),
+    ([1, 0], 0, 1, "one", 1, 2, 1),
+]
+
+
+@pytest.mark.parametrize("case", BRUTE, ids=lambda c: f"{c[0]}-p{c[1]}-{c[3]}-k{c[4]}-n{c[5]}")
+def test_brute_force_every_injective_assignment(case):
+    is_mla, path, sep, grouping, cmin, n, pf = case
+    d = small_desc(is_mla, path, sep, grouping, cmin, pf)
+    probe = oracle.Layout(dict(d, pool_bytes=1 << 30)).summary
+    footprint = probe["pool_bytes_used"] // probe["num_blocks"]
+    need = n * probe["n_kv_groups"] * probe["blocks_per_chunk"]
+    # a pool of 4-8 blocks: the enumeration stays small and reaches the pool end
+    d["pool_bytes"] = max(4, min(8, need + 1)) * footprint + 3
+    lay = oracle.Layout(d)
+    s = lay.summary
+    nb = s["num_blocks"]
+    assert need <= nb <= 8
+    rng = np.random.default_rng(11)
+    used = s["pool_bytes_used"]
+    pool = rng.integers(0, 256, used, dtype=np.uint8)
+    count = 0
+    for perm in itertools.permutations(range(nb), need):
+        ids = np.asarray(perm, np.int32).reshape(n, lay.G, lay.k)
+        objs = [[np.zeros(lay.obj_bytes(o), np.uint8) for o in range(lay.O)] for _ in range(n)]
+        lay.store(pool, ids, objs)
+        ref = objects_by_views(s, lay.layers, pool, ids)
+        for c in range(n):
+            for o in range(lay.O):
+                assert np.array_equal(objs[c][o], ref[c][o])
+        lo = np.zeros(used, np.uint8)
+        hi = np.full(used, 0xFF, np.uint8)
+        lay.retrieve(lo, ids, objs)
+        lay.retrieve(hi, ids, objs)
+        written = (lo != 0) | (hi != 0xFF)
+        assert int(written.sum()) == payload_bytes(s, n)
+        assert np.array_equal(pool[written], lo[written]), "retrieve(store(x)) at the same ids"
+        count += 1
+    assert count > 0
+
+
+# ---------------------------------------------------------------- errors
+def test_id_range_and_alias_errors():
+    d = small_desc([0, 0, 1], 0, 1, "default", 1, 2)
+    lay = oracle.Layout(d)
+    s = lay.summary
+    pool = np.zeros(s["pool_bytes_used"], np.uint8)
+    objs = [[np.zeros(lay.obj_bytes(o), np.uint8) for o in range(lay.O)] for _ in range(2)]
+    nb = s["num_blocks"]
+    ids = np.arange(2 * lay.G * lay.k, dtype=np.int32).reshape(2, lay.G, lay.k) % nb
+    bad = ids.copy()
+    bad[1, 0, 0] = nb
+    for fn in (lay.store, lay.retrieve):
+        with pytest.raises(oracle.OracleError) as e:
+            fn(pool, bad, objs)
+        assert e.value.status == oracle.E_RANGE
+        bad[1, 0, 0] = -1
+        with pytest.raises(oracle.OracleError) as e:
+            fn(pool, bad, objs)
+        assert e.value.status == oracle.E_RANGE
+        bad[1, 0, 0] = nb
+    dup = ids.copy()
+    dup[1, 0, 0] = dup[0, 0, 0]
+    lay.store(pool, dup, objs)  # repeated sources are fine
+    with pytest.raises(oracle.OracleError) as e:
+        lay.retrieve(pool, dup, objs)
+    assert e.value.status == oracle.E_ALIAS
+    # an empty call is a no-op
+    lay.store(pool, np.zeros((0, lay.G, lay.k), np.int32), [])
+    lay.retrieve(pool, np.zeros((0, lay.G, lay.k), np.int32), [])
+
+
+def test_pool_too_small():
+    d = small_desc([0, 1], 0, 1, "default", 1, 1)
+    d["pool_bytes"] = 10
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.Layout(d)
+    assert e.value.status == oracle.E_POOL

@@ -1,0 +1,361 @@
+"""Seeded synthetic inputs for chunk store/retrieve.
+
+The oracle side and the HIP side both draw their inputs from here, and from
+nowhere else.  The module holds none of the method's arithmetic: no page
+sizes, offsets, block-size or chunk rules.  It holds only:
+
+1. SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+   generators", OOPSLA 2014), used as a counter-based byte generator.  Word q
+   of a buffer with seed s is ``mix64(s + (q + 1) * GAMMA)``, little-endian.
+   Because any word can be computed from its index alone, a large pool can be
+   filled on the GPU (``workloads.gpu_fill``) and any sampled range checked on
+   the host.
+2. Fisher-Yates permutations of block ids, drawn from a SplitMix64 stream.
+3. The five workload descriptions: model shapes, pool sizes and request mix.
+4. Planning of waves of whole requests, given the pool's block count and the
+   number of block ids each chunk needs (both read back from a layout).
+"""
+from __future__ import annotations
+
+import copy
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+import numpy as np
+
+GAMMA = 0x9E3779B97F4A7C15
+MASK = (1 << 64) - 1
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+FILL_LIB_PATH = os.path.join(HERE, "libhkvfill.so")
+
+
+# --------------------------------------------------------------------------
+# SplitMix64
+# --------------------------------------------------------------------------
+def mix64_int(z: int) -> int:
+    """SplitMix64's output function on one 64-bit integer (pure Python)."""
+    z &= MASK
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & MASK
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & MASK
+    return z ^ (z >> 31)
+
+
+def mix64(z: np.ndarray) -> np.ndarray:
+    """SplitMix64's output function, vectorised over a uint64 array."""
+    z = z.astype(np.uint64, copy=True)
+    with np.errstate(over="ignore"):
+        z ^= z >> np.uint64(30)
+        z *= np.uint64(0xBF58476D1CE4E5B9)
+        z ^= z >> np.uint64(27)
+        z *= np.uint64(0x94D049BB133111EB)
+        z ^= z >> np.uint64(31)
+    return z
+
+
+def words(seed: int, start: int, count: int) -> np.ndarray:
+    """Words [start, start+count) of the counter-based stream with this seed."""
+    q = np.arange(start + 1, start + 1 + count, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        x = np.uint64(seed & MASK) + q * np.uint64(GAMMA)
+    return mix64(x)
+
+
+def fill_bytes(seed: int, byte_start: int, nbytes: int) -> np.ndarray:
+    """Bytes [byte_start, byte_start+nbytes) of the stream, as uint8."""
+    if nbytes <= 0:
+        return np.zeros(0, dtype=np.uint8)
+    w0 = byte_start // 8
+    w1 = (byte_start + nbytes + 7) // 8
+    w = words(seed, w0, w1 - w0).astype("<u8", copy=False)
+    b = w.view(np.uint8)
+    off = byte_start - w0 * 8
+    return b[off:off + nbytes].copy()
+
+
+class Stream:
+    """A sequential SplitMix64 stream (state += GAMMA; output mix64(state))."""
+
+    def __init__(self, seed: int):
+        self.state = seed & MASK
+
+    def next(self) -> int:
+        self.state = (self.state + GAMMA) & MASK
+        return mix64_int(self.state)
+
+
+def derive_seed(*parts: int) -> int:
+    """A seed for a named sub-stream: folds the integer parts through mix64."""
+    h = 0
+    for p in parts:
+        h = mix64_int((h + (p & MASK) * GAMMA + 0x2545F4914F6CDD1D) & MASK)
+    return h
+
+
+def permutation(seed: int, n: int) -> np.ndarray:
+    """Fisher-Yates shuffle of range(n) driven by a SplitMix64 stream: for i
+    from n-1 down to 1, swap element i with element next() % (i+1)."""
+    perm = list(range(n))
+    s = Stream(seed)
+    for i in range(n - 1, 0, -1):
+        j = s.next() % (i + 1)
+        perm[i], perm[j] = perm[j], perm[i]
+    return np.asarray(perm, dtype=np.int32)
+
+
+# Sub-stream tags.
+TAG_POOL, TAG_OBJ, TAG_STORE_IDS, TAG_RETRIEVE_IDS, TAG_REQUESTS, TAG_SHARED_IDS = 1, 2, 3, 4, 5, 6
+
+
+# --------------------------------------------------------------------------
+# GPU fill (same stream definition, for pools too large to copy from host)
+# --------------------------------------------------------------------------
+_fill_lib = None
+
+
+def _load_fill():
+    global _fill_lib
+    if _fill_lib is None:
+        if not os.path.exists(FILL_LIB_PATH):
+            raise RuntimeError(f"{FILL_LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(FILL_LIB_PATH)
+        L.hkvfill_splitmix.restype = ctypes.c_int
+        L.hkvfill_splitmix.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
+                                       ctypes.c_uint64, ctypes.c_void_p]
+        _fill_lib = L
+    return _fill_lib
+
+
+def gpu_fill(dev_ptr: int, nbytes: int, seed: int, byte_start: int = 0, stream: int = 0) -> None:
+    """Fill nbytes of device memory at dev_ptr with stream bytes
+    [byte_start, byte_start+nbytes) of `seed`.  byte_start must be a multiple
+    of 8 and dev_ptr 8-byte aligned."""
+    if nbytes == 0:
+        return
+    if byte_start % 8 or dev_ptr % 8:
+        raise ValueError("gpu_fill needs 8-byte aligned start and pointer")
+    rc = _load_fill().hkvfill_splitmix(dev_ptr, nbytes, seed & MASK, byte_start // 8, stream)
+    if rc != 0:
+        raise RuntimeError(f"gpu fill failed with HIP error {rc}")
+
+
+# --------------------------------------------------------------------------
+# Workload descriptions
+# --------------------------------------------------------------------------
+GIB = 1 << 30
+MIB = 1 << 20
+
+
+def kkkm_pattern(n_layers: int, tail_mla: int = 0) -> list:
+    """Layer types for the "three KDA layers then one MLA layer" pattern
+    (1 = MLA), with `tail_mla` extra MLA layers at the end.  Kimi-Linear's 27
+    layers: kkkm_pattern(24) + [0, 0, 1]; K3's 93: kkkm_pattern(92, 1)."""
+    return [1 if i % 4 == 3 else 0 for i in range(n_layers)] + [1] * tail_mla
+
+
+KIMI_LINEAR_27 = kkkm_pattern(24) + [0, 0, 1]
+K3_93 = kkkm_pattern(92, tail_mla=1)
+
+
+def _desc(is_mla, heads, head_dim, conv_dim, mla_bytes, path, pool_bytes, block_size=0,
+          chunk_min=1, kv_group_of_layer=None, separate=1, state_bytes=4, conv_kernel=4,
+          conv_bytes=2, mla_width=576, strict=0, max_batched=0) -> dict:
+    return dict(is_mla=list(is_mla), kda_heads=heads, kda_head_dim=head_dim,
+                kda_state_bytes=state_bytes, conv_dim=conv_dim, conv_kernel=conv_kernel,
+                conv_bytes=conv_bytes, mla_width=mla_width, mla_bytes=mla_bytes,
+                block_size=block_size, chunk_min_tokens=chunk_min, strict_chunk_multiple=strict,
+                path=path, separate_object_groups=separate,
+                kv_group_of_layer=kv_group_of_layer, pool_bytes=pool_bytes,
+                max_num_batched_tokens=max_batched)
+
+
+@dataclass
+class Phase:
+    op: str                       # "store" or "retrieve"
+    chunks: list                  # [(request, chunk_index)] in request then chunk order
+    prefilled_objects: bool = False  # retrieve of objects that no store in this run made
+
+
+@dataclass
+class Config:
+    name: str
+    title: str
+    desc: dict
+    requests: list                # chunks per request
+    phases: list                  # [Phase]
+    seed: int
+    shared_permutation: bool = False  # all phases draw ids from one permutation
+    notes: str = ""
+    extra: dict = field(default_factory=dict)
+
+
+def _all_chunks(requests, first=None):
+    out = []
+    for r, n in enumerate(requests):
+        m = n if first is None else min(first, n)
+        out += [(r, c) for c in range(m)]
+    return out
+
+
+def _tiny_requests(seed: int) -> list:
+    s = Stream(derive_seed(seed, TAG_REQUESTS))
+    return [3 + s.next() % 3 for _ in range(4)]
+
+
+def make_config(name: str) -> Config:
+    """The five workloads at full size."""
+    if name == "tiny":
+        seed = 0x48B0001
+        req = _tiny_requests(seed)
+        # 4 layers KKKM; 2 heads x 16 x 16 fp32 + (96, 3) bf16; bf16 MLA;
+        # path A pool of 64 blocks of the unified page (64 x 16 x 576 x 2 B).
+        desc = _desc([0, 0, 0, 1], 2, 16, 96, 2, 0, 64 * 16 * 576 * 2)
+        return Config(name, "Tiny: 4 layers (3 KDA + 1 MLA), path A, 64 blocks", desc, req,
+                      [Phase("store", _all_chunks(req)), Phase("retrieve", _all_chunks(req))],
+                      seed)
+    if name == "kl_tp2":
+        seed = 0x48B0002
+        req = [8] * 64
+        desc = _desc(KIMI_LINEAR_27, 16, 128, 6144, 2, 0, 16 * GIB)
+        return Config(name, "Kimi-Linear-48B-A3B, one TP=2 rank, path A, 16 GiB pool", desc,
+                      req, [Phase("store", _all_chunks(req)),
+                            Phase("retrieve", _all_chunks(req))], seed)
+    if name == "kl_tp1":
+        seed = 0x48B0003
+        req = [8] * 128
+        desc = _desc(KIMI_LINEAR_27, 32, 128, 12288, 2, 1, 64 * GIB)
+        return Config(name, "Kimi-Linear full state (TP=1), path B, 64 GiB pool", desc, req,
+                      [Phase("store", _all_chunks(req)),
+                       Phase("retrieve", _all_chunks(req, first=4))], seed,
+                      notes="128 requests of 16k tokens = 8 whole chunks each; the retrieve "
+                            "hits the first 4 chunks of every request (50% prefix hits)")
+    if name == "k3_tp8":
+        seed = 0x48B0004
+        req = [4] * 256
+        desc = _desc(K3_93, 6, 128, 2304, 1, 0, 24 * GIB, block_size=768, chunk_min=1500)
+        return Config(name, "K3-shaped TP=8 rank, path A, fp8 MLA, N=768, chunk min 1500, "
+                      "24 GiB pool", desc, req,
+                      [Phase("store", _all_chunks(req)), Phase("retrieve", _all_chunks(req))],
+                      seed)
+    if name == "long_ctx":
+        seed = 0x48B0005
+        req = [530] + [1] * 512
+        desc = _desc(KIMI_LINEAR_27, 32, 128, 12288, 2, 1, 100 * GIB)
+        return Config(name, "Long context: 530-chunk prefix retrieve + 512 tail stores, "
+                      "path B, 100 GiB pool", desc, req,
+                      [Phase("retrieve", [(0, c) for c in range(530)], prefilled_objects=True),
+                       Phase("store", [(r, 0) for r in range(1, 513)])],
+                      seed, shared_permutation=True,
+                      notes="a 1,000,000-token prefix is 530 whole chunks of 1888 tokens; each "
+                            "2k-token request has one whole chunk")
+    raise KeyError(name)
+
+
+CONFIG_NAMES = ("tiny", "kl_tp2", "kl_tp1", "k3_tp8", "long_ctx")
+
+
+def make_small_config(name: str) -> Config:
+    """The same page shapes with a smaller pool and fewer requests, so the
+    oracle finishes in seconds; still several waves, several tiles per page
+    and ragged sub-tiles."""
+    cfg = copy.deepcopy(make_config(name))
+    if name == "tiny":
+        return cfg
+    if name == "kl_tp2":
+        cfg.desc["pool_bytes"] = 512 * MIB
+        cfg.requests = [3] * 6
+        cfg.phases = [Phase("store", _all_chunks(cfg.requests)),
+                      Phase("retrieve", _all_chunks(cfg.requests))]
+    elif name == "kl_tp1":
+        cfg.desc["pool_bytes"] = 1 * GIB
+        cfg.requests = [4] * 5
+        cfg.phases = [Phase("store", _all_chunks(cfg.requests)),
+                      Phase("retrieve", _all_chunks(cfg.requests, first=2))]
+    elif name == "k3_tp8":
+        cfg.desc["pool_bytes"] = 512 * MIB
+        cfg.requests = [2] * 7
+        cfg.phases = [Phase("store", _all_chunks(cfg.requests)),
+                      Phase("retrieve", _all_chunks(cfg.requests))]
+    elif name == "long_ctx":
+        cfg.desc["pool_bytes"] = 1 * GIB
+        cfg.requests = [8] + [1] * 8
+        cfg.phases = [Phase("retrieve", [(0, c) for c in range(8)], prefilled_objects=True),
+                      Phase("store", [(r, 0) for r in range(1, 9)])]
+    cfg.name = name + "_small"
+    return cfg
+
+
+# --------------------------------------------------------------------------
+# Waves and block tables
+# --------------------------------------------------------------------------
+@dataclass
+class Wave:
+    op: str
+    chunks: list          # [(request, chunk_index)]
+    ids: np.ndarray       # int32 [n_chunks][G][k]
+    pool_seed: int | None  # store waves: the pool is (re)filled with this seed first
+    prefilled_objects: bool = False
+
+
+def object_seed(cfg: Config, request: int, chunk: int) -> int:
+    return derive_seed(cfg.seed, TAG_OBJ, request, chunk)
+
+
+def _split_waves(chunks, max_chunks: int):
+    """Greedy waves of whole requests, each at most max_chunks chunks."""
+    if max_chunks < 1:
+        raise ValueError("the pool cannot hold one chunk's blocks")
+    waves, cur, cur_req = [], [], None
+    by_req = {}
+    for rc in chunks:
+        by_req.setdefault(rc[0], []).append(rc)
+    for r in sorted(by_req):
+        group = by_req[r]
+        if len(group) > max_chunks:
+            raise ValueError("a request has more chunks than the pool holds at once")
+        if len(cur) + len(group) > max_chunks:
+            waves.append(cur)
+            cur = []
+        cur = cur + group
+        cur_req = r
+    if cur:
+        waves.append(cur)
+    del cur_req
+    return waves
+
+
+def plan_waves(cfg: Config, num_blocks: int, n_kv_groups: int, blocks_per_chunk: int) -> list:
+    """Block tables for every wave.  Ids are assigned from a Fisher-Yates
+    permutation of [0, num_blocks) in request order, chunk order, KV-group
+    order, then block order; every wave of a phase draws a fresh permutation
+    (fresh, fragmented ids), or all phases share one permutation when the
+    config says so."""
+    ids_per_chunk = n_kv_groups * blocks_per_chunk
+    max_chunks = num_blocks // ids_per_chunk
+    waves = []
+    shared = None
+    shared_pos = 0
+    if cfg.shared_permutation:
+        shared = permutation(derive_seed(cfg.seed, TAG_SHARED_IDS), num_blocks)
+    for pi, ph in enumerate(cfg.phases):
+        for wi, chunks in enumerate(_split_waves(ph.chunks, max_chunks)):
+            need = len(chunks) * ids_per_chunk
+            if shared is not None:
+                if shared_pos + need > num_blocks:
+                    raise ValueError("phases sharing one permutation do not fit the pool")
+                flat = shared[shared_pos:shared_pos + need]
+                shared_pos += need
+            else:
+                tag = TAG_STORE_IDS if ph.op == "store" else TAG_RETRIEVE_IDS
+                flat = permutation(derive_seed(cfg.seed, tag, pi, wi), num_blocks)[:need]
+            ids = flat.reshape(len(chunks), n_kv_groups, blocks_per_chunk).copy()
+            pool_seed = None
+            if ph.op == "store" and not cfg.shared_permutation:
+                pool_seed = derive_seed(cfg.seed, TAG_POOL, pi, wi)
+            waves.append(Wave(ph.op, chunks, ids, pool_seed, ph.prefilled_objects))
+    return waves
+
+
+def initial_pool_seed(cfg: Config) -> int:
+    return derive_seed(cfg.seed, TAG_POOL, 0xFFFF)
