@@ -1,0 +1,241 @@
+"""Store+retrieve throughput of KV/state pages on one MI355X.
+
+One step is one pass of the whole hot path over one batch: every wave of the
+workload (for the Kimi-Linear TP=1 workload: store 1024 chunks = 128 requests
+x 8 chunks of 1888 tokens, then retrieve the first 4 chunks of every request
+into freshly drawn, fragmented block ids).  Inputs (pool, objects, block
+tables) are seeded, synthetic and resident in HBM before timing starts.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "store+retrieve GB/s of KV/state pages (Kimi-Linear shapes, N=1888); % HBM peak"
+COPY_SRC = os.path.join(ROOT, "retrieve_store_chunk_amd", "csrc", "hkv_copy.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    with open(COPY_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(config: str, tile: int, max_wg: int):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source
+    and launch configuration; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if (t.get("kernel_sha") != kernel_source_sha() or t.get("tile_bytes", 0) != tile
+            or t.get("max_workgroups", 0) != max_wg):
+        return None
+    return t.get("store_gather_bytes_per_launch")
+
+
+def cpu_baseline(cfg, min_seconds: float = 10.0, max_seconds: float = 30.0) -> dict:
+    """The oracle (plain C, one thread, one memcpy per page) on a bounded
+    sample of the same workload: the same layout shapes in a smaller pool,
+    64 chunks stored and their first halves retrieved into fresh ids,
+    repeated until at least min_seconds of CPU time."""
+    import numpy as np
+    import oracle
+    import workloads as W
+
+    desc = dict(cfg.desc)
+    lay_full = oracle.Layout(desc)
+    per_block = lay_full.summary["pool_bytes_used"] // lay_full.summary["num_blocks"]
+    n_store = 64
+    ids_per_chunk = lay_full.G * lay_full.k
+    desc["pool_bytes"] = per_block * (n_store * ids_per_chunk + 1)
+    lay = oracle.Layout(desc)
+    s = lay.summary
+    pool = np.full(s["pool_bytes_used"], 0x5A, np.uint8)
+    objs = [[np.full(lay.obj_bytes(o), 0xA5, np.uint8) for o in range(lay.O)]
+            for _ in range(n_store)]
+    perm = W.permutation(W.derive_seed(cfg.seed, 1234), s["num_blocks"])
+    store_ids = perm[: n_store * ids_per_chunk].reshape(n_store, lay.G, lay.k)
+    perm2 = W.permutation(W.derive_seed(cfg.seed, 1235), s["num_blocks"])
+    n_ret = n_store // 2
+    ret_ids = perm2[: n_ret * ids_per_chunk].reshape(n_ret, lay.G, lay.k)
+    payload = (n_store + n_ret) * (s["obj_bytes0"] + s["obj_bytes1"])
+    passes, t_cpu = 0, 0.0
+    while t_cpu < min_seconds and (passes == 0 or t_cpu + t_cpu / passes < max_seconds):
+        c0 = time.perf_counter()
+        lay.store(pool, store_ids, objs)
+        lay.retrieve(pool, ret_ids, objs[:n_ret])
+        t_cpu += time.perf_counter() - c0
+        passes += 1
+    gbs = passes * payload / t_cpu / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} passes of: store {n_store} chunks + retrieve {n_ret} chunks "
+                      f"(same page shapes, pool of {s['num_blocks']} blocks); "
+                      f"{passes * payload / 1e9:.1f} GB moved in {t_cpu:.1f} s wall, "
+                      "single-threaded plain C memcpy"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="kl_tp1",
+                    help="workload: tiny, kl_tp2, kl_tp1 (default), k3_tp8, long_ctx")
+    ap.add_argument("--tile-bytes", type=int, default=0)
+    ap.add_argument("--max-workgroups", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-ceiling", action="store_true",
+                    help="also time a plain device-to-device copy of the same bytes")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the store/retrieve path has no cross-GPU "
+              "step in this build; run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as W
+    from workloads.driver import GpuWorkload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    cfg = W.make_config(args.config)
+    log(f"workload {cfg.name}: {cfg.title}")
+    g = GpuWorkload(cfg, tile_bytes=args.tile_bytes, max_workgroups=args.max_workgroups)
+    info = g.info
+    log(f"layout: N={info['block_size']} C={info['chunk_tokens']} k={info['blocks_per_chunk']} "
+        f"blocks={info['num_blocks']} stride={info['block_stride']} "
+        f"chunk payload={info['chunk_payload_bytes']} B; {len(g.waves)} waves")
+    g.init_pool()
+    g.fill_objects(W.derive_seed(cfg.seed, 77))
+    g.prefill_objects()
+    torch.cuda.synchronize()
+    log("inputs resident in HBM")
+
+    stream = g.stream
+    n_w = len(g.waves)
+    per_wave_payload = [len(w.chunks) * info["chunk_payload_bytes"] for w in g.waves]
+    step_payload = sum(per_wave_payload)
+
+    def one_step(events=None):
+        for i, w in enumerate(g.waves):
+            if events is not None:
+                events[i][0].record(stream)
+            g.run_wave(w)
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(n_w)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        one_step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = step_payload / (ms_per_step / 1e3) / 1e9
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} GB/s")
+
+    # per-kernel: each call enqueues one tiny table upload and one launch
+    kern = {}
+    for i, w in enumerate(g.waves):
+        name = "hkv_store_gather" if w.op == "store" else "hkv_retrieve_scatter"
+        ms = [evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]
+        k = kern.setdefault(name, {"launches": 0, "ms": 0.0, "payload": 0})
+        k["launches"] += args.steps
+        k["ms"] += sum(ms)
+        k["payload"] += per_wave_payload[i] * args.steps
+    kernels = {}
+    for name, k in kern.items():
+        avg_ms = k["ms"] / k["launches"]
+        bytes_per_launch = 2 * k["payload"] / k["launches"]  # read + write of every page
+        kernels[name] = {"launches_per_step": k["launches"] // args.steps,
+                         "avg_ms": round(avg_ms, 4),
+                         "hbm_bytes_per_launch": int(bytes_per_launch),
+                         "hbm_GBs": round(bytes_per_launch / (avg_ms / 1e3) / 1e9, 1)}
+    dom = max(kernels, key=lambda n: kernels[n]["hbm_bytes_per_launch"] *
+              kernels[n]["launches_per_step"])
+    achieved = kernels[dom]["hbm_GBs"]
+    traffic = load_traffic(args.config, args.tile_bytes, args.max_workgroups) \
+        if dom == "hkv_store_gather" else None
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "title": cfg.title,
+                   "chunks_per_step": sum(len(w.chunks) for w in g.waves),
+                   "payload_bytes_per_step": step_payload,
+                   "block_size": info["block_size"], "chunk_tokens": info["chunk_tokens"],
+                   "path": "B packed" if info["path"] else "A padded-unified",
+                   "tile_bytes": args.tile_bytes, "max_workgroups": args.max_workgroups},
+        "pct_hbm_peak": round(100 * 2 * value / HBM_PEAK_GBS, 2),
+        "chunks_per_s": round(sum(len(w.chunks) for w in g.waves) / (ms_per_step / 1e3), 1),
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+
+    if args.copy_ceiling:
+        n = min(8 << 30, g.pool.numel() // 2)
+        a, b = g.pool[:n], g.pool[n:2 * n]
+        for _ in range(3):
+            b.copy_(a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        out["copy_ceiling"] = {"bytes": n, "avg_ms": round(ms, 4),
+                               "hbm_GBs": round(2 * n / (ms / 1e3) / 1e9, 1),
+                               "what": "torch copy_ of one contiguous buffer (read + write)"}
+        log(f"copy ceiling: {out['copy_ceiling']['hbm_GBs']} GB/s")
+
+    del g
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(cfg)
+        log(f"cpu baseline: {out['cpu_baseline']['value']} GB/s")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

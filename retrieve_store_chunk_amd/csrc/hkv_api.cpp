@@ -1,0 +1,320 @@
+// C ABI of the chunk store/retrieve library (declared in include/hkv.h).
+//
+// Per call: validate everything on the host, write the call's tables (layer
+// placements, work items, block ids, object addresses) into a pinned staging
+// slot, copy them into the caller's workspace on the caller's stream, and
+// launch one gather or scatter kernel on the same stream.  No call
+// synchronises the stream; a staging slot is reused only after the event
+// recorded behind its copy has completed.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "hkv.h"
+#include "hkv_device_tables.hpp"
+#include "hkv_launch.hpp"
+#include "hkv_plan.hpp"
+
+struct hkv_layout {
+  hkv::Plan plan;
+};
+
+namespace {
+
+thread_local std::string t_last_error;
+
+hkv_status set_error(hkv_status st, const std::string& msg) {
+  t_last_error = msg;
+  return st;
+}
+
+hkv_status hip_error(hipError_t e, const char* what) {
+  return set_error(HKV_E_HIP, std::string(what) + ": " + hipGetErrorName(e) + " (" +
+                                  hipGetErrorString(e) + ")");
+}
+
+// ---------------------------------------------------------------- staging
+// A few pinned host buffers per device, used round-robin.  Each remembers
+// the event recorded after the copy that reads it.
+constexpr int kSlots = 8;
+
+struct Slot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t done = nullptr;
+  bool pending = false;
+};
+
+struct Ring {
+  std::mutex mu;
+  Slot slot[kSlots];
+  unsigned next = 0;
+};
+
+std::mutex g_rings_mu;
+std::map<int, std::unique_ptr<Ring>>* g_rings = new std::map<int, std::unique_ptr<Ring>>();
+
+Ring* ring_for(int dev) {
+  std::lock_guard<std::mutex> g(g_rings_mu);
+  auto& r = (*g_rings)[dev];
+  if (!r) r.reset(new Ring());
+  return r.get();
+}
+
+// Makes `dev` current for the scope, restoring the previous device after.
+struct DeviceScope {
+  int prev = -1;
+  hipError_t err = hipSuccess;
+  explicit DeviceScope(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
+  }
+  ~DeviceScope() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+// Copies `bytes` bytes of `fill`-written staging into `dst` on `stream`.
+template <class Fill>
+hkv_status upload(void* dst, size_t bytes, hipStream_t stream, Fill fill) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_error(e, "finding the stream's device");
+  DeviceScope scope(dev);
+  if (scope.err != hipSuccess) return hip_error(scope.err, "selecting the stream's device");
+  Ring* ring = ring_for(dev);
+  std::lock_guard<std::mutex> g(ring->mu);
+  Slot& s = ring->slot[ring->next++ % kSlots];
+  if (s.pending) {
+    e = hipEventSynchronize(s.done);
+    if (e != hipSuccess) return hip_error(e, "waiting for a staging slot");
+    s.pending = false;
+  }
+  if (s.cap < bytes) {
+    if (s.host) {
+      e = hipHostFree(s.host);
+      s.host = nullptr;
+      s.cap = 0;
+      if (e != hipSuccess) return hip_error(e, "hipHostFree (staging)");
+    }
+    const size_t cap = std::max<size_t>(bytes, size_t(64) << 10);
+    e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_error(e, "hipHostMalloc (staging)");
+    s.cap = cap;
+  }
+  if (!s.done) {
+    e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_error(e, "hipEventCreate (staging)");
+  }
+  fill(static_cast<uint8_t*>(s.host));
+  e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_error(e, "hipMemcpyAsync (tables)");
+  e = hipEventRecord(s.done, stream);
+  if (e != hipSuccess) return hip_error(e, "hipEventRecord (staging)");
+  s.pending = true;
+  return HKV_OK;
+}
+
+// ---------------------------------------------------------------- validation
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  uintptr_t lo, hi;
+  const char* what;
+};
+
+hkv_status check_disjoint(std::vector<Span>& spans) {
+  std::sort(spans.begin(), spans.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i].lo < spans[i - 1].hi)
+      return set_error(HKV_E_ALIAS, std::string(spans[i - 1].what) + " overlaps " +
+                                        spans[i].what);
+  return HKV_OK;
+}
+
+hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
+                    const hkv_chunk_batch* b, void* ws, size_t ws_bytes, void* stream) {
+  if (!layout || !b) return set_error(HKV_E_ARG, "layout and batch must not be NULL");
+  if (b->n_chunks < 0) return set_error(HKV_E_ARG, "n_chunks must be >= 0");
+  if (b->n_chunks == 0) return HKV_OK;
+  if (!pool || !b->block_ids || !b->objects)
+    return set_error(HKV_E_ARG, "pool, block_ids and objects must not be NULL");
+  const hkv::Plan& p = layout->plan;
+  const uint64_t n = (uint64_t)b->n_chunks;
+  const uint64_t G = (uint64_t)p.n_kv_groups, k = (uint64_t)p.blocks_per_chunk;
+  const uint64_t O = (uint64_t)p.n_obj_groups;
+  const uint64_t per_chunk = p.items.size();
+  if (n * per_chunk > 0x7FFFFFFFull)
+    return set_error(HKV_E_ARG, "too many tiles in one call; split the batch");
+  const hkv::WorkspaceLayout wl =
+      hkv::workspace_layout(p.dev_layers.size(), per_chunk, n, G, k, O);
+  if (!ws || ws_bytes < wl.total)
+    return set_error(HKV_E_WORKSPACE, "workspace needs " + std::to_string(wl.total) + " bytes");
+  if (!aligned16(pool)) return set_error(HKV_E_ALIGN, "pool pointer is not 16-byte aligned");
+  if (!aligned16(ws)) return set_error(HKV_E_ALIGN, "workspace is not 16-byte aligned");
+  for (uint64_t i = 0; i < n * O; ++i) {
+    if (!b->objects[i]) return set_error(HKV_E_ARG, "object pointer is NULL");
+    if (!aligned16(b->objects[i]))
+      return set_error(HKV_E_ALIGN, "object pointer is not 16-byte aligned");
+  }
+  const int32_t* ids = b->block_ids;
+  const uint64_t n_ids = n * G * k;
+  for (uint64_t i = 0; i < n_ids; ++i)
+    if (ids[i] < 0 || ids[i] >= p.num_blocks)
+      return set_error(HKV_E_RANGE, "block id " + std::to_string(ids[i]) + " outside [0, " +
+                                        std::to_string(p.num_blocks) + ")");
+  if (!store) {
+    // One block-id space for all groups: distinct ids <=> disjoint writes.
+    std::vector<uint8_t> seen((size_t)p.num_blocks, 0);
+    for (uint64_t i = 0; i < n_ids; ++i) {
+      if (seen[(size_t)ids[i]])
+        return set_error(HKV_E_ALIAS, "retrieve target block id " + std::to_string(ids[i]) +
+                                          " appears twice in one call");
+      seen[(size_t)ids[i]] = 1;
+    }
+  }
+  std::vector<Span> spans;
+  spans.reserve(n * O + 2);
+  const uintptr_t pb = reinterpret_cast<uintptr_t>(pool);
+  spans.push_back({pb, pb + p.pool_used, "the pool"});
+  const uintptr_t wb = reinterpret_cast<uintptr_t>(ws);
+  spans.push_back({wb, wb + wl.total, "the workspace"});
+  for (uint64_t c = 0; c < n; ++c)
+    for (uint64_t o = 0; o < O; ++o) {
+      const uintptr_t a = reinterpret_cast<uintptr_t>(b->objects[c * O + o]);
+      if (p.obj_bytes[o]) spans.push_back({a, a + p.obj_bytes[o], "an object"});
+    }
+  hkv_status st = check_disjoint(spans);
+  if (st != HKV_OK) return st;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  st = upload(ws, wl.total, s, [&](uint8_t* h) {
+    std::memcpy(h + wl.layers_off, p.dev_layers.data(), p.dev_layers.size() * sizeof(hkv::DevLayer));
+    std::memcpy(h + wl.items_off, p.items.data(), per_chunk * sizeof(uint64_t));
+    std::memcpy(h + wl.ids_off, ids, n_ids * sizeof(int32_t));
+    uint64_t* objs = reinterpret_cast<uint64_t*>(h + wl.objs_off);
+    for (uint64_t i = 0; i < n * O; ++i) objs[i] = reinterpret_cast<uintptr_t>(b->objects[i]);
+  });
+  if (st != HKV_OK) return st;
+
+  hkv::CopyArgs a{};
+  a.pool = static_cast<uint8_t*>(const_cast<void*>(pool));
+  a.layers = reinterpret_cast<const hkv::DevLayer*>(wsb + wl.layers_off);
+  a.items = reinterpret_cast<const uint64_t*>(wsb + wl.items_off);
+  a.ids = reinterpret_cast<const int32_t*>(wsb + wl.ids_off);
+  a.objs = reinterpret_cast<const uint64_t*>(wsb + wl.objs_off);
+  a.total_items = n * per_chunk;
+  a.tile_bytes = p.tile_bytes;
+  a.items_per_chunk = (uint32_t)per_chunk;
+  a.n_kv_groups = (uint32_t)G;
+  a.blocks_per_chunk = (uint32_t)k;
+  a.n_obj_groups = (uint32_t)O;
+  uint64_t grid = a.total_items;
+  if (p.max_workgroups && grid > p.max_workgroups) grid = p.max_workgroups;
+  const int e = hkv::launch_copy(store, a, (uint32_t)grid, stream);
+  if (e != 0) return hip_error((hipError_t)e, store ? "launching hkv_store_gather"
+                                                    : "launching hkv_retrieve_scatter");
+  return HKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hkv_status hkv_unified_block_size(const hkv_model* model, int32_t align_tokens, int64_t* n_out) {
+  if (!model || !n_out) return set_error(HKV_E_ARG, "model and n_out must not be NULL");
+  if (align_tokens != 0 && align_tokens != 16)
+    return set_error(HKV_E_ARG, "only a 16-token step is supported");
+  std::string err;
+  hkv_status st = hkv::unified_block_size(*model, n_out, &err);
+  return st == HKV_OK ? st : set_error(st, err);
+}
+
+hkv_status hkv_layout_init(const hkv_layout_desc* desc, hkv_layout** out) {
+  if (!desc || !out) return set_error(HKV_E_ARG, "desc and out must not be NULL");
+  std::unique_ptr<hkv_layout> lay(new (std::nothrow) hkv_layout());
+  if (!lay) return set_error(HKV_E_ARG, "out of host memory");
+  std::string err;
+  hkv_status st = hkv::make_plan(*desc, &lay->plan, &err);
+  if (st != HKV_OK) return set_error(st, err);
+  *out = lay.release();
+  return HKV_OK;
+}
+
+void hkv_layout_destroy(hkv_layout* layout) { delete layout; }
+
+hkv_status hkv_layout_info_get(const hkv_layout* layout, hkv_layout_info* out) {
+  if (!layout || !out) return set_error(HKV_E_ARG, "layout and out must not be NULL");
+  const hkv::Plan& p = layout->plan;
+  std::memset(out, 0, sizeof(*out));
+  out->block_size = p.block_size;
+  out->chunk_tokens = p.chunk_tokens;
+  out->blocks_per_chunk = p.blocks_per_chunk;
+  out->n_layers = (int32_t)p.layers.size();
+  out->n_kv_groups = p.n_kv_groups;
+  out->n_obj_groups = p.n_obj_groups;
+  out->num_blocks = p.num_blocks;
+  out->path = p.path;
+  out->n_slabs = p.n_slabs;
+  out->unified_page_bytes = p.unified_page;
+  out->block_stride = p.block_stride;
+  out->pool_bytes_used = p.pool_used;
+  out->obj_bytes[0] = p.obj_bytes[0];
+  out->obj_bytes[1] = p.obj_bytes[1];
+  out->chunk_payload_bytes = p.obj_bytes[0] + p.obj_bytes[1];
+  return HKV_OK;
+}
+
+hkv_status hkv_layer_info_get(const hkv_layout* layout, int32_t layer, hkv_layer_info* out) {
+  if (!layout || !out) return set_error(HKV_E_ARG, "layout and out must not be NULL");
+  const hkv::Plan& p = layout->plan;
+  if (layer < 0 || layer >= (int32_t)p.layers.size())
+    return set_error(HKV_E_ARG, "layer index out of range");
+  const hkv::LayerPlacement& x = p.layers[layer];
+  out->is_mla = x.is_mla;
+  out->kv_group = x.kv_group;
+  out->obj_group = x.obj_group;
+  out->slot = x.slot;
+  out->page_bytes = x.page;
+  out->reserved_bytes = x.reserved;
+  out->pool_offset = x.pool_offset;
+  out->stride = x.stride;
+  out->obj_offset = x.obj_offset;
+  return HKV_OK;
+}
+
+hkv_status hkv_workspace_size(const hkv_layout* layout, int32_t max_chunks, size_t* bytes) {
+  if (!layout || !bytes) return set_error(HKV_E_ARG, "layout and bytes must not be NULL");
+  if (max_chunks < 0) return set_error(HKV_E_ARG, "max_chunks must be >= 0");
+  const hkv::Plan& p = layout->plan;
+  *bytes = (size_t)hkv::workspace_layout(p.dev_layers.size(), p.items.size(),
+                                         (uint64_t)max_chunks, (uint64_t)p.n_kv_groups,
+                                         (uint64_t)p.blocks_per_chunk,
+                                         (uint64_t)p.n_obj_groups)
+               .total;
+  return HKV_OK;
+}
+
+hkv_status hkv_store_chunks(const hkv_layout* layout, const void* pool,
+                            const hkv_chunk_batch* batch, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  return run_copy(true, layout, pool, batch, workspace, ws_bytes, stream);
+}
+
+hkv_status hkv_retrieve_chunks(const hkv_layout* layout, void* pool,
+                               const hkv_chunk_batch* batch, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  return run_copy(false, layout, pool, batch, workspace, ws_bytes, stream);
+}
+
+const char* hkv_last_error(void) { return t_last_error.c_str(); }
+
+}  // extern "C"

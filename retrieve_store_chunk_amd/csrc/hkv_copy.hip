@@ -1,0 +1,118 @@
+// Gather (store) and scatter (retrieve) kernels for CDNA4 (gfx950).
+//
+// The work of a call is a flat list of tiles: every (chunk, layer, block j,
+// tile s) is one span of at most tile_bytes contiguous bytes on both sides,
+// because a page is contiguous in the pool (vLLM hybrid KV-cache blog,
+// sections 3.1 and 3.2: a layer's page sits at offset + block_id * stride)
+// and in the object.  A workgroup takes one tile at a time:
+//   - the tile's table entries (work item, layer placement, block id, object
+//     address) are uniform across the workgroup and are read through the
+//     constant address space, so they land in SGPRs (scalar loads);
+//   - the bytes move as 16-byte vectors per lane, 64 lanes of a wave
+//     covering 1 KiB contiguous, kUnroll loads in flight per lane before the
+//     matching stores, with nontemporal hints (the pools are far larger than
+//     the caches, nothing is reused);
+//   - only real page bytes are touched, so KDA padding (path A) and group
+//     slack (path B) are never read or written.
+// A page is opaque bytes ("Kimi-Linear" recipe: the KDA state is an opaque
+// page), so data only ever lives in integer vector registers: NaN payloads
+// of bf16/fp8 values pass unchanged.
+#include <hip/hip_runtime.h>
+
+#include "hkv_device_tables.hpp"
+#include "hkv_launch.hpp"
+
+#define HKV_GLOBAL __attribute__((address_space(1)))
+#define HKV_CONST __attribute__((address_space(4)))
+
+namespace {
+
+constexpr uint32_t kThreads = hkv::kCopyThreads;
+constexpr uint32_t kUnroll = 4;
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// Copies `bytes` bytes from src to dst with all kThreads lanes of the
+// workgroup.  Spans whose pointers and length are 16-byte multiples take the
+// vector path; anything else (pages whose size is not a 16-byte multiple)
+// falls back to byte copies.
+__device__ __forceinline__ void copy_span(uint8_t* dst, const uint8_t* src, uint32_t bytes) {
+  const uint32_t t = threadIdx.x;
+  if (((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src) | bytes) & 15u) ==
+      0) {
+    const HKV_GLOBAL v4u* s = (const HKV_GLOBAL v4u*)src;
+    HKV_GLOBAL v4u* d = (HKV_GLOBAL v4u*)dst;
+    const uint32_t n = bytes >> 4;
+    constexpr uint32_t kStep = kThreads * kUnroll;
+    uint32_t base = 0;
+    for (; base + kStep <= n; base += kStep) {
+      v4u v[kUnroll];
+#pragma unroll
+      for (uint32_t u = 0; u < kUnroll; ++u)
+        v[u] = __builtin_nontemporal_load(s + base + u * kThreads + t);
+#pragma unroll
+      for (uint32_t u = 0; u < kUnroll; ++u)
+        __builtin_nontemporal_store(v[u], d + base + u * kThreads + t);
+    }
+    for (uint32_t i = base + t; i < n; i += kThreads)
+      __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
+  } else {
+    const HKV_GLOBAL uint8_t* s = (const HKV_GLOBAL uint8_t*)src;
+    HKV_GLOBAL uint8_t* d = (HKV_GLOBAL uint8_t*)dst;
+    for (uint32_t i = t; i < bytes; i += kThreads) d[i] = s[i];
+  }
+}
+
+template <bool kStore>
+__device__ __forceinline__ void copy_items(const hkv::CopyArgs& a) {
+  const HKV_CONST hkv::DevLayer* layers = (const HKV_CONST hkv::DevLayer*)a.layers;
+  const HKV_CONST uint64_t* items = (const HKV_CONST uint64_t*)a.items;
+  const HKV_CONST int32_t* ids = (const HKV_CONST int32_t*)a.ids;
+  const HKV_CONST uint64_t* objs = (const HKV_CONST uint64_t*)a.objs;
+  const uint32_t total = (uint32_t)a.total_items;
+  for (uint32_t item = blockIdx.x; item < total; item += gridDim.x) {
+    const uint32_t c = item / a.items_per_chunk;
+    const uint32_t r = item - c * a.items_per_chunk;
+    const uint64_t w = items[r];
+    const uint32_t l = (uint32_t)(w & 0xFFFFu);
+    const uint32_t j = (uint32_t)((w >> 16) & 0xFFFFu);
+    const uint32_t s = (uint32_t)(w >> 32);
+    const HKV_CONST hkv::DevLayer* L = layers + l;
+    const uint64_t page_bytes = L->page;
+    const int64_t id = ids[((uint64_t)c * a.n_kv_groups + L->kv_group) * a.blocks_per_chunk + j];
+    uint8_t* obj = reinterpret_cast<uint8_t*>(objs[(uint64_t)c * a.n_obj_groups + L->obj_group]);
+    const uint64_t off = (uint64_t)s * a.tile_bytes;
+    const uint64_t rest = page_bytes - off;
+    const uint32_t bytes = (uint32_t)(rest < a.tile_bytes ? rest : a.tile_bytes);
+    uint8_t* page = a.pool + L->pool_offset + (uint64_t)id * L->stride + off;
+    uint8_t* dst_obj = obj + L->obj_offset + (uint64_t)j * page_bytes + off;
+    if (kStore)
+      copy_span(dst_obj, page, bytes);
+    else
+      copy_span(page, dst_obj, bytes);
+  }
+}
+
+}  // namespace
+
+extern "C" __global__ __launch_bounds__(kThreads) void hkv_store_gather(hkv::CopyArgs a) {
+  copy_items<true>(a);
+}
+
+extern "C" __global__ __launch_bounds__(kThreads) void hkv_retrieve_scatter(hkv::CopyArgs a) {
+  copy_items<false>(a);
+}
+
+namespace hkv {
+
+int launch_copy(bool store, const CopyArgs& a, uint32_t grid, void* stream) {
+  if (grid == 0) return 0;
+  CopyArgs arg = a;
+  void* params[] = {&arg};
+  const void* fn = store ? reinterpret_cast<const void*>(&hkv_store_gather)
+                         : reinterpret_cast<const void*>(&hkv_retrieve_scatter);
+  return (int)hipLaunchKernel(fn, dim3(grid), dim3(kThreads), params, 0,
+                              reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // namespace hkv

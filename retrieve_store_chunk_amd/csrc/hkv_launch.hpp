@@ -1,0 +1,17 @@
+// Host-side entry to the copy kernels.
+#pragma once
+
+#include <cstdint>
+
+#include "hkv_device_tables.hpp"
+
+namespace hkv {
+
+constexpr uint32_t kCopyThreads = 256;
+
+// Enqueues the gather (store) or scatter (retrieve) kernel over
+// a.total_items work items with `grid` workgroups on `stream` (a
+// hipStream_t).  Returns the hipError_t of the launch (0 = success).
+int launch_copy(bool store, const CopyArgs& a, uint32_t grid, void* stream);
+
+}  // namespace hkv

@@ -1,0 +1,176 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+- libhkv exports every function include/hkv.h declares;
+- its planner gives the same layout as the oracle's for the five workloads
+  and for random small layouts (including identical error codes);
+- argument validation rejects bad calls before any HIP call.  These use
+  fake device addresses, so they run only where no GPU is visible; the GPU
+  suite repeats the error paths with real buffers.
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+import oracle
+import retrieve_store_chunk_amd as hkv
+import workloads
+from tests.test_oracle_pins import layout_params, small_desc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "hkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hkv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert {"hkv_unified_block_size", "hkv_layout_init", "hkv_store_chunks",
+            "hkv_retrieve_chunks"} <= set(names)
+    for n in names:
+        assert hasattr(hkv.lib, n), n
+
+
+def same_plan(desc):
+    ref = oracle.Layout(desc)
+    got = hkv.Layout(desc)
+    s, i = ref.summary, got.info
+    assert i["block_size"] == s["block_size"]
+    assert i["chunk_tokens"] == s["chunk_tokens"]
+    assert i["blocks_per_chunk"] == s["blocks_per_chunk"]
+    assert i["num_blocks"] == s["num_blocks"]
+    assert i["n_layers"] == s["n_layers"]
+    assert i["n_kv_groups"] == s["n_kv_groups"]
+    assert i["n_obj_groups"] == s["n_obj_groups"]
+    assert i["path"] == s["path"]
+    assert i["n_slabs"] == s["n_slabs"]
+    assert i["unified_page_bytes"] == s["unified_page_bytes"]
+    assert i["block_stride"] == s["block_stride"]
+    assert i["pool_bytes_used"] == s["pool_bytes_used"]
+    assert i["obj_bytes"] == [s["obj_bytes0"], s["obj_bytes1"]]
+    assert i["chunk_payload_bytes"] == s["obj_bytes0"] + s["obj_bytes1"]
+    for a, b in zip(got.layers, ref.layers):
+        for key in oracle.LAYER_FIELDS:
+            assert a[key] == b[key], key
+    return got
+
+
+@pytest.mark.parametrize("name", workloads.CONFIG_NAMES)
+def test_planner_matches_oracle_on_workloads(name):
+    same_plan(workloads.make_config(name).desc)
+    same_plan(workloads.make_small_config(name).desc)
+
+
+def test_unified_block_size_matches_oracle():
+    for name in workloads.CONFIG_NAMES:
+        d = workloads.make_config(name).desc
+        kda = oracle.kda_page_bytes(d["kda_heads"], d["kda_head_dim"], d["kda_state_bytes"],
+                                    d["conv_dim"], d["conv_kernel"], d["conv_bytes"])
+        n_ref = oracle.unified_block_size(kda, d["mla_width"] * d["mla_bytes"])
+        assert hkv.hkv_unified_block_size(d) == n_ref
+    d = workloads.make_config("kl_tp2").desc
+    assert hkv.hkv_unified_block_size(d) == 944
+    assert hkv.status_of(hkv.hkv_unified_block_size, d, 8) == hkv.HKV_E_ARG
+
+
+def status_oracle(desc):
+    try:
+        oracle.Layout(desc)
+        return 0
+    except oracle.OracleError as e:
+        return e.status
+
+
+@settings(max_examples=200, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(layout_params, st.sampled_from([0, 16, 48, 64, 100]), st.integers(0, 1),
+       st.sampled_from([0, 15, 16, 17, 31, 32, 100]))
+def test_planner_matches_oracle_on_random_layouts(params, block_size, strict, budget):
+    is_mla, path, sep, grouping, cmin, pf, conv = params
+    d = small_desc(is_mla, path, sep, grouping, cmin, pf, conv_dim=conv)
+    d.update(block_size=block_size, strict_chunk_multiple=strict, max_num_batched_tokens=budget)
+    st_ref = status_oracle(d)
+    st_got = hkv.status_of(hkv.hkv_layout_init, d)
+    assert st_got == st_ref
+    if st_ref == 0:
+        same_plan(d)
+
+
+def test_layout_errors_match_oracle():
+    base = workloads.make_config("kl_tp2").desc
+    cases = [dict(block_size=928), dict(block_size=950), dict(chunk_min_tokens=0),
+             dict(chunk_min_tokens=1000, strict_chunk_multiple=1), dict(pool_bytes=1000),
+             dict(max_num_batched_tokens=100), dict(path=2),
+             dict(kv_group_of_layer=[0] * 26 + [2]), dict(kv_group_of_layer=[-1] * 27)]
+    for c in cases:
+        d = dict(base, **c)
+        assert hkv.status_of(hkv.hkv_layout_init, d) == status_oracle(d) != 0, c
+    # knobs the oracle does not have
+    for c in (dict(tile_bytes=1000), dict(tile_bytes=(1 << 30) + 4096)):
+        assert hkv.status_of(hkv.hkv_layout_init, dict(base, **c)) == hkv.HKV_E_ARG
+
+
+def test_workspace_size_grows_with_chunks():
+    lay = hkv.Layout(workloads.make_config("kl_tp1").desc)
+    a, b = lay.workspace_size(1), lay.workspace_size(1024)
+    assert 0 < a < b and a % 256 == 0 and b % 256 == 0
+    assert hkv.status_of(hkv.hkv_workspace_size, lay.handle, -1) == hkv.HKV_E_ARG
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake device addresses: host-only check")
+def test_call_validation_on_host():
+    lay = hkv.Layout(workloads.make_config("tiny").desc)
+    G, k, O = lay.G, lay.k, lay.O
+    nb = lay.info["num_blocks"]
+    pool = 1 << 40
+    used = lay.info["pool_bytes_used"]
+    obj0 = pool + (1 << 30)
+    objs = [obj0 + i * (1 << 20) for i in range(2 * O)]
+    ws_bytes = lay.workspace_size(2)
+    ws = pool + (1 << 32)
+    ids = np.arange(2 * G * k, dtype=np.int32).reshape(2, G, k)
+
+    def st(fn, **kw):
+        a = dict(pool=pool, ids=ids, objs=objs, ws=ws, ws_bytes=ws_bytes)
+        a.update(kw)
+        return hkv.status_of(fn, lay.handle, a["pool"], a["ids"], a["objs"], a["ws"],
+                             a["ws_bytes"], 0)
+
+    for fn in (hkv.hkv_store_chunks, hkv.hkv_retrieve_chunks):
+        assert st(fn, ws_bytes=ws_bytes - 1) == hkv.HKV_E_WORKSPACE
+        assert st(fn, ws=0) == hkv.HKV_E_WORKSPACE
+        assert st(fn, pool=pool + 8) == hkv.HKV_E_ALIGN
+        assert st(fn, ws=ws + 4) == hkv.HKV_E_ALIGN
+        assert st(fn, objs=[objs[0] + 1] + objs[1:]) == hkv.HKV_E_ALIGN
+        assert st(fn, objs=[0] + objs[1:]) == hkv.HKV_E_ARG
+        bad = ids.copy()
+        bad[1, 0, 0] = nb
+        assert st(fn, ids=bad) == hkv.HKV_E_RANGE
+        bad[1, 0, 0] = -1
+        assert st(fn, ids=bad) == hkv.HKV_E_RANGE
+        # overlapping objects / object inside the pool / workspace in the pool
+        assert st(fn, objs=[objs[0]] * len(objs)) == hkv.HKV_E_ALIAS
+        assert st(fn, objs=[pool + used - 256] + objs[1:]) == hkv.HKV_E_ALIAS
+        assert st(fn, ws=pool) == hkv.HKV_E_ALIAS
+        # an empty batch is a no-op even with NULL pointers
+        assert hkv.status_of(fn, lay.handle, 0, np.zeros((0, G, k), np.int32), [], 0, 0,
+                             0) == hkv.HKV_OK
+    dup = ids.copy()
+    dup[1, 0, 0] = dup[0, 0, 0]
+    assert st(hkv.hkv_retrieve_chunks, ids=dup) == hkv.HKV_E_ALIAS
+    assert hkv.status_of(hkv.hkv_store_chunks, 0, pool, ids, objs, ws, ws_bytes, 0) \
+        == hkv.HKV_E_ARG
+    assert "workspace" in hkv.hkv_last_error() or hkv.hkv_last_error() != ""

@@ -1,0 +1,209 @@
+"""GPU parity: the HIP library against the CPU oracle, byte for byte.
+
+Every case runs the same seeded waves on both sides and compares the whole
+pool after every wave and every object at the end.  Inputs are generated on
+the host (workloads.fill_bytes) and copied to the device, so neither side's
+inputs come from the other.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def run_parity(cfg, tile_bytes=0, max_workgroups=0, pool_fill=None):
+    from workloads.driver import GpuWorkload
+    _log(f"[parity] {cfg.name} tile={tile_bytes} max_wg={max_workgroups}")
+    g = GpuWorkload(cfg, tile_bytes=tile_bytes, max_workgroups=max_workgroups)
+    ref = oracle.Layout(cfg.desc)
+    for key, okey in (("num_blocks", "num_blocks"), ("pool_bytes_used", "pool_bytes_used"),
+                      ("n_kv_groups", "n_kv_groups"), ("blocks_per_chunk", "blocks_per_chunk")):
+        assert g.info[key] == ref.summary[okey]
+    used = ref.summary["pool_bytes_used"]
+    O = ref.O
+
+    def upload_pool(seed):
+        host = pool_fill(used, seed) if pool_fill else W.fill_bytes(seed, 0, used)
+        g.pool[:used].copy_(torch.from_numpy(host))
+        torch.cuda.synchronize()
+        return host
+
+    pool_ref = upload_pool(W.initial_pool_seed(cfg))
+    objs_ref = {}
+    for rc in g.slot_of:
+        objs_ref[rc] = []
+        for o in range(O):
+            a = W.fill_bytes(W.derive_seed(W.object_seed(cfg, *rc), o), 0, ref.obj_bytes(o))
+            objs_ref[rc].append(a)
+            g.object_view(rc, o).copy_(torch.from_numpy(a))
+    torch.cuda.synchronize()
+    for i, w in enumerate(g.waves):
+        if w.op == "store" and w.pool_seed is not None:
+            pool_ref = upload_pool(w.pool_seed)
+        g.run_wave(w)
+        g.stream.synchronize()
+        objs = [objs_ref[rc] for rc in w.chunks]
+        (ref.store if w.op == "store" else ref.retrieve)(pool_ref, w.ids, objs)
+        got = g.host_pool()
+        assert np.array_equal(got, pool_ref), f"pool differs after wave {i} ({w.op})"
+    for rc in g.slot_of:
+        for o in range(O):
+            got = g.host_object(rc, o)
+            assert np.array_equal(got, objs_ref[rc][o]), f"object {rc}/{o} differs"
+    n_waves = len(g.waves)
+    del g
+    torch.cuda.empty_cache()
+    return n_waves
+
+
+@pytest.mark.parametrize("name", W.CONFIG_NAMES)
+def test_workload_parity_small(name):
+    """The five workloads with their real page shapes, smaller pools and
+    fewer requests: several waves, several tiles per page, ragged last tiles."""
+    n = run_parity(W.make_small_config(name))
+    assert n >= 2
+
+
+@pytest.mark.parametrize("tile,max_wg", [(4096, 0), (8192, 7), (1 << 20, 1), (1 << 30, 3),
+                                         (0, 13)])
+def test_results_do_not_depend_on_tuning(tile, max_wg):
+    run_parity(W.make_config("tiny"), tile_bytes=tile, max_workgroups=max_wg)
+    run_parity(W.make_small_config("k3_tp8"), tile_bytes=tile, max_workgroups=max_wg)
+
+
+def pathological(nbytes, seed):
+    """bf16 / fp8 NaNs with payloads, infinities, -0, denormals, mixed with
+    random bytes: a copy through float registers would change some."""
+    pats = np.array([0x7FC1, 0xFFFF, 0x7F81, 0x8000, 0x0001, 0x807F, 0x7F80, 0xFF80,
+                     0x7F7F, 0xFFFE], dtype="<u2").view(np.uint8)
+    out = W.fill_bytes(seed, 0, nbytes)
+    reps = np.resize(pats, nbytes // 2 * 2)
+    out[: reps.size: 2] = reps[::2]
+    out[1: reps.size: 2] = np.where(np.arange(reps.size // 2) % 3 == 0,
+                                    out[1: reps.size: 2], reps[1::2])
+    return out
+
+
+def test_pathological_bit_patterns():
+    run_parity(W.make_config("tiny"), pool_fill=pathological)
+    run_parity(W.make_small_config("k3_tp8"), pool_fill=pathological)
+
+
+def mini_config(name, is_mla, path, sep=1, grouping=None, chunk_min=1, conv_dim=4,
+                mla_width=8, mla_bytes=1, heads=1, head_dim=4, blocks=12, requests=(2, 1, 3),
+                retrieve_first=None):
+    """A small layout with a given shape; the pool holds `blocks` blocks."""
+    desc = W._desc(is_mla, heads, head_dim, conv_dim, mla_bytes, path, 1 << 30,
+                   chunk_min=chunk_min, kv_group_of_layer=grouping, separate=sep,
+                   mla_width=mla_width)
+    probe = oracle.Layout(desc).summary
+    per_block = probe["pool_bytes_used"] // probe["num_blocks"]
+    desc["pool_bytes"] = blocks * per_block + 5
+    req = list(requests)
+    store = W._all_chunks(req)
+    retr = W._all_chunks(req, first=retrieve_first)
+    return W.Config(name, name, desc, req, [W.Phase("store", store), W.Phase("retrieve", retr)],
+                    seed=W.derive_seed(len(name), sum(is_mla), path))
+
+
+EDGE = [
+    # page sizes that are not 16-byte multiples (byte path) and odd offsets
+    mini_config("odd_pages_A", [0, 0, 1], 0, conv_dim=5),
+    mini_config("odd_pages_B", [0, 1, 0, 1], 1, conv_dim=5, mla_width=9),
+    # several blocks per chunk
+    mini_config("k3_blocks", [0, 1, 0], 0, chunk_min=40, blocks=30),
+    # one object holding every layer; one group holding every layer
+    mini_config("merged_objects", [0, 0, 0, 1], 1, sep=0),
+    mini_config("one_group", [0, 1, 1, 0], 1, grouping=[0, 0, 0, 0], blocks=8),
+    mini_config("group_per_layer", [1, 0, 1], 0, grouping=[2, 0, 1], blocks=12,
+                requests=(1, 1, 1, 1)),
+    # a single layer, only KDA, only MLA
+    mini_config("single_mla", [1], 0, blocks=5, requests=(2, 3)),
+    mini_config("only_kda", [0, 0, 0], 1, blocks=9),
+    mini_config("only_mla", [1, 1], 1, blocks=6, requests=(3, 3)),
+    # pages of several tiles (4096-byte tiles) with a ragged end
+    mini_config("multi_tile", [0, 0, 1], 1, heads=3, head_dim=40, conv_dim=104, mla_width=320,
+                mla_bytes=2, blocks=10),
+    # the whole pool addressed: every id up to num_blocks - 1 is used
+    mini_config("full_pool", [0, 0, 0, 1], 0, blocks=8, requests=(1, 1)),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=lambda c: c.name)
+def test_edge_layouts(cfg):
+    run_parity(cfg)
+    run_parity(cfg, tile_bytes=4096, max_workgroups=3)
+
+
+def test_empty_batch_is_a_noop():
+    import retrieve_store_chunk_amd as hkv
+    from workloads.driver import GpuWorkload
+    g = GpuWorkload(W.make_config("tiny"))
+    g.init_pool()
+    before = g.host_pool().copy()
+    empty = np.zeros((0, g.layout.G, g.layout.k), np.int32)
+    hkv.hkv_store_chunks(g.layout.handle, g.pool.data_ptr(), empty, [], g.ws.data_ptr(),
+                         g.ws_bytes, g.stream.cuda_stream)
+    hkv.hkv_retrieve_chunks(g.layout.handle, g.pool.data_ptr(), empty, [], g.ws.data_ptr(),
+                            g.ws_bytes, g.stream.cuda_stream)
+    assert np.array_equal(g.host_pool(), before)
+
+
+def test_error_paths_enqueue_nothing():
+    import retrieve_store_chunk_amd as hkv
+    from workloads.driver import GpuWorkload
+    g = GpuWorkload(W.make_config("tiny"))
+    g.init_pool()
+    g.fill_objects(5)
+    g.stream.synchronize()
+    pool0 = g.host_pool().copy()
+    w = g.waves[0]
+    ptrs = g.object_ptrs(w.chunks)
+    h, s = g.layout.handle, g.stream.cuda_stream
+    P, WS = g.pool.data_ptr(), g.ws.data_ptr()
+    nb = g.info["num_blocks"]
+    bad = w.ids.copy()
+    bad[-1, -1, -1] = nb
+    cases = [
+        (hkv.hkv_retrieve_chunks, (h, P, bad, ptrs, WS, g.ws_bytes, s), hkv.HKV_E_RANGE),
+        (hkv.hkv_store_chunks, (h, P, bad, ptrs, WS, g.ws_bytes, s), hkv.HKV_E_RANGE),
+        (hkv.hkv_retrieve_chunks, (h, P + 8, w.ids, ptrs, WS, g.ws_bytes, s), hkv.HKV_E_ALIGN),
+        (hkv.hkv_retrieve_chunks, (h, P, w.ids, ptrs, WS, 16, s), hkv.HKV_E_WORKSPACE),
+        (hkv.hkv_store_chunks, (h, P, w.ids, [ptrs[0]] * len(ptrs), WS, g.ws_bytes, s),
+         hkv.HKV_E_ALIAS),
+    ]
+    if len(w.chunks) > 1:
+        dup = w.ids.copy()
+        dup[1, 0, 0] = dup[0, 0, 0]
+        cases.append((hkv.hkv_retrieve_chunks, (h, P, dup, ptrs, WS, g.ws_bytes, s),
+                      hkv.HKV_E_ALIAS))
+    for fn, args, want in cases:
+        assert hkv.status_of(fn, *args) == want
+    g.stream.synchronize()
+    assert np.array_equal(g.host_pool(), pool0)
+
+
+def test_gpu_fill_matches_host_generator():
+    t = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    for seed, start, n in [(1, 0, 1 << 20), (0x48B0003, 4096, 12345), (7, 8, 7)]:
+        W.gpu_fill(t.data_ptr(), n, seed, start)
+        torch.cuda.synchronize()
+        assert np.array_equal(t[:n].cpu().numpy(), W.fill_bytes(seed, start, n))

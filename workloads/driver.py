@@ -1,0 +1,130 @@
+"""Runs a workload through the HIP library: torch for device memory and
+streams, the product binding for every store/retrieve.  No oracle here.
+
+Object storage: one device tensor per object group with one slot per
+(request, chunk) that any phase touches; slot rows are 256-byte aligned.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import retrieve_store_chunk_amd as hkv
+import workloads as W
+
+
+def _align(x: int, a: int = 256) -> int:
+    return (x + a - 1) // a * a
+
+
+class GpuWorkload:
+    def __init__(self, cfg: W.Config, device: str = "cuda:0", tile_bytes: int = 0,
+                 max_workgroups: int = 0, stream: torch.cuda.Stream | None = None):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        desc = dict(cfg.desc, tile_bytes=tile_bytes, max_workgroups=max_workgroups)
+        self.layout = hkv.Layout(desc)
+        info = self.layout.info
+        self.info = info
+        self.waves = W.plan_waves(cfg, info["num_blocks"], self.layout.G, self.layout.k)
+        self.stream = stream if stream is not None else torch.cuda.Stream(device=self.device)
+        # object slots
+        self.slot_of = {}
+        for ph in cfg.phases:
+            for rc in ph.chunks:
+                self.slot_of.setdefault(rc, len(self.slot_of))
+        n_slots = len(self.slot_of)
+        self.obj_stride = [_align(max(1, info["obj_bytes"][o])) for o in range(self.layout.O)]
+        self.pool = torch.empty(_align(info["pool_bytes_used"]), dtype=torch.uint8,
+                                device=self.device)
+        self.objs = [torch.empty(n_slots * self.obj_stride[o], dtype=torch.uint8,
+                                 device=self.device) for o in range(self.layout.O)]
+        max_chunks = max((len(w.chunks) for w in self.waves), default=0)
+        self.ws_bytes = self.layout.workspace_size(max_chunks)
+        self.ws = torch.empty(max(256, self.ws_bytes), dtype=torch.uint8, device=self.device)
+        self.pool_seed_of = {}   # (r, c) -> seed of the pool its store read
+        self.store_ids = {}      # (r, c) -> [G][k] block ids its store read
+
+    # ------------------------------------------------------------ addresses
+    def object_ptrs(self, chunks) -> list:
+        out = []
+        for rc in chunks:
+            s = self.slot_of[rc]
+            for o in range(self.layout.O):
+                out.append(self.objs[o].data_ptr() + s * self.obj_stride[o])
+        return out
+
+    def object_view(self, rc, o) -> torch.Tensor:
+        s = self.slot_of[rc]
+        return self.objs[o][s * self.obj_stride[o]: s * self.obj_stride[o]
+                            + self.info["obj_bytes"][o]]
+
+    # ------------------------------------------------------------ fills
+    def fill_pool(self, seed: int) -> None:
+        with torch.cuda.stream(self.stream):
+            W.gpu_fill(self.pool.data_ptr(), self.pool.numel(), seed, 0,
+                       self.stream.cuda_stream)
+
+    def fill_objects(self, seed: int) -> None:
+        with torch.cuda.stream(self.stream):
+            for o in range(self.layout.O):
+                W.gpu_fill(self.objs[o].data_ptr(), self.objs[o].numel(),
+                           W.derive_seed(seed, o), 0, self.stream.cuda_stream)
+
+    def prefill_objects(self) -> None:
+        """Objects that a retrieve reads without an earlier store in this run
+        hold seeded bytes: object group o of (r, c) is the stream
+        derive_seed(object_seed(r, c), o)."""
+        for w in self.waves:
+            if w.op == "retrieve" and w.prefilled_objects:
+                for rc in w.chunks:
+                    for o in range(self.layout.O):
+                        v = self.object_view(rc, o)
+                        W.gpu_fill(v.data_ptr(), v.numel(),
+                                   W.derive_seed(W.object_seed(self.cfg, *rc), o), 0,
+                                   self.stream.cuda_stream)
+
+    # ------------------------------------------------------------ calls
+    def run_wave(self, w: W.Wave) -> None:
+        ptrs = self.object_ptrs(w.chunks)
+        fn = self.layout.store if w.op == "store" else self.layout.retrieve
+        fn(self.pool.data_ptr(), w.ids, ptrs, self.ws.data_ptr(), self.ws_bytes,
+           self.stream.cuda_stream)
+
+    def run_all(self, on_wave=None) -> None:
+        """Every wave in order.  A store wave with a pool seed first refills
+        the pool with it.  Records, per stored chunk, the seed of the pool
+        it read and its block ids."""
+        self.prefill_objects()
+        for i, w in enumerate(self.waves):
+            if w.op == "store" and w.pool_seed is not None:
+                self.fill_pool(w.pool_seed)
+                self.current_pool_seed = w.pool_seed
+            if w.op == "store":
+                for n, rc in enumerate(w.chunks):
+                    self.pool_seed_of[rc] = self.current_pool_seed
+                    self.store_ids[rc] = w.ids[n].copy()
+            self.run_wave(w)
+            if on_wave is not None:
+                self.stream.synchronize()
+                on_wave(i, w)
+
+    current_pool_seed = None
+
+    def init_pool(self) -> int:
+        seed = W.initial_pool_seed(self.cfg)
+        self.fill_pool(seed)
+        self.current_pool_seed = seed
+        return seed
+
+    def payload_bytes(self, waves=None) -> int:
+        waves = self.waves if waves is None else waves
+        return sum(len(w.chunks) for w in waves) * self.info["chunk_payload_bytes"]
+
+    def host_pool(self) -> np.ndarray:
+        self.stream.synchronize()
+        return self.pool[: self.info["pool_bytes_used"]].cpu().numpy()
+
+    def host_object(self, rc, o) -> np.ndarray:
+        self.stream.synchronize()
+        return self.object_view(rc, o).cpu().numpy()
