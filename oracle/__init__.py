@@ -16,7 +16,7 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.environ.get("HKVREF_LIB") or os.path.join(HERE, "libhkvref.so")
+LIB_PATH = os.path.join(HERE, "libhkvref.so")
 
 DESC_KEYS = (
     "is_mla", "kda_heads", "kda_head_dim", "kda_state_bytes", "conv_dim", "conv_kernel",
@@ -42,31 +42,35 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             from . import build as _build  # noqa: F401  (build on first use)
             _build.build()
-        L = ctypes.CDLL(LIB_PATH)
-        i32, i64, u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
-        vp = ctypes.c_void_p
-        L.hkvref_kda_page_bytes.restype = i64
-        L.hkvref_kda_page_bytes.argtypes = [i32] * 6
-        L.hkvref_unified_block_size.restype = ctypes.c_int
-        L.hkvref_unified_block_size.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
-        L.hkvref_chunk_tokens.restype = ctypes.c_int
-        L.hkvref_chunk_tokens.argtypes = [i64, i64, i32, ctypes.POINTER(i64)]
-        L.hkvref_layout_init.restype = ctypes.c_int
-        L.hkvref_layout_init.argtypes = [i32, vp, i32, i32, i32, i32, i32, i32, i32, i32,
-                                         i64, i64, i32, i32, i32, vp, u64, i64,
-                                         ctypes.POINTER(vp)]
-        L.hkvref_layout_free.restype = None
-        L.hkvref_layout_free.argtypes = [vp]
-        L.hkvref_layout_summary.restype = ctypes.c_int
-        L.hkvref_layout_summary.argtypes = [vp, ctypes.POINTER(i64)]
-        L.hkvref_layer.restype = ctypes.c_int
-        L.hkvref_layer.argtypes = [vp, i32, ctypes.POINTER(i64)]
-        L.hkvref_store_chunks.restype = ctypes.c_int
-        L.hkvref_store_chunks.argtypes = [vp, vp, i32, vp, vp]
-        L.hkvref_retrieve_chunks.restype = ctypes.c_int
-        L.hkvref_retrieve_chunks.argtypes = [vp, vp, i32, vp, vp]
-        _lib = L
+        _lib = bind(ctypes.CDLL(LIB_PATH))
     return _lib
+
+
+def bind(L: ctypes.CDLL) -> ctypes.CDLL:
+    """Declares the C signatures on a loaded build of hkvref.c."""
+    i32, i64, u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+    vp = ctypes.c_void_p
+    L.hkvref_kda_page_bytes.restype = i64
+    L.hkvref_kda_page_bytes.argtypes = [i32] * 6
+    L.hkvref_unified_block_size.restype = ctypes.c_int
+    L.hkvref_unified_block_size.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
+    L.hkvref_chunk_tokens.restype = ctypes.c_int
+    L.hkvref_chunk_tokens.argtypes = [i64, i64, i32, ctypes.POINTER(i64)]
+    L.hkvref_layout_init.restype = ctypes.c_int
+    L.hkvref_layout_init.argtypes = [i32, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                     i64, i64, i32, i32, i32, vp, u64, i64,
+                                     ctypes.POINTER(vp)]
+    L.hkvref_layout_free.restype = None
+    L.hkvref_layout_free.argtypes = [vp]
+    L.hkvref_layout_summary.restype = ctypes.c_int
+    L.hkvref_layout_summary.argtypes = [vp, ctypes.POINTER(i64)]
+    L.hkvref_layer.restype = ctypes.c_int
+    L.hkvref_layer.argtypes = [vp, i32, ctypes.POINTER(i64)]
+    L.hkvref_store_chunks.restype = ctypes.c_int
+    L.hkvref_store_chunks.argtypes = [vp, vp, i32, vp, vp]
+    L.hkvref_retrieve_chunks.restype = ctypes.c_int
+    L.hkvref_retrieve_chunks.argtypes = [vp, vp, i32, vp, vp]
+    return L
 
 
 def kda_page_bytes(heads, head_dim, state_bytes, conv_dim, conv_kernel, conv_bytes) -> int:
@@ -118,6 +122,7 @@ class Layout:
 
     def __init__(self, desc: dict):
         L = lib()
+        self._L = L
         is_mla = np.ascontiguousarray(np.asarray(desc["is_mla"], dtype=np.uint8))
         kvg = desc.get("kv_group_of_layer")
         kvg_arr = None if kvg is None else np.ascontiguousarray(np.asarray(kvg, dtype=np.int32))
@@ -146,8 +151,8 @@ class Layout:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and _lib is not None:
-            _lib.hkvref_layout_free(h)
+        if h is not None and self._L is not None:
+            self._L.hkvref_layout_free(h)
             self._h = None
 
     @property
@@ -187,7 +192,7 @@ class Layout:
         n = ids.shape[0] if ids.ndim else 0
         addrs = _ptr_array(objects, n, self.O)
         self._check_buffers(pool, objects)
-        rc = lib().hkvref_store_chunks(self._h, pool.ctypes.data, n, ids.ctypes.data, addrs)
+        rc = self._L.hkvref_store_chunks(self._h, pool.ctypes.data, n, ids.ctypes.data, addrs)
         if rc != OK:
             raise OracleError(rc, "store_chunks")
 
@@ -196,6 +201,6 @@ class Layout:
         n = ids.shape[0] if ids.ndim else 0
         addrs = _ptr_array(objects, n, self.O)
         self._check_buffers(pool, objects)
-        rc = lib().hkvref_retrieve_chunks(self._h, pool.ctypes.data, n, ids.ctypes.data, addrs)
+        rc = self._L.hkvref_retrieve_chunks(self._h, pool.ctypes.data, n, ids.ctypes.data, addrs)
         if rc != OK:
             raise OracleError(rc, "retrieve_chunks")

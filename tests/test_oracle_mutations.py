@@ -1,0 +1,129 @@
+"""The pins catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of oracle/hkvref.c (on the CPU), builds
+it, points the oracle wrapper at it, and runs the pins of
+test_oracle_pins.py until one fails.  A mutant that passes every pin would
+mean the pins do not fix that part of the oracle.
+"""
+import ctypes
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+from tests import golden_io
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "hkvref.c")
+
+# name -> (original text, planted mistake)
+MUTANTS = {
+    "slab_base_ignores_num_blocks": (
+        "lay->pool_offset[l] = (int64_t)lay->index_in_group[l] * lay->num_blocks * p;",
+        "lay->pool_offset[l] = (int64_t)lay->index_in_group[l] * p;"),
+    "path_b_offset_not_a_prefix_sum": (
+        "                lay->pool_offset[l] = byte_offset;\n"
+        "                byte_offset += lay->page[l];",
+        "                byte_offset += lay->page[l];\n"
+        "                lay->pool_offset[l] = byte_offset - lay->page[0];"),
+    "object_block_offset_uses_stride": (
+        "uint8_t* dst = obj + lay->obj_offset[l] + j * lay->page[l];",
+        "uint8_t* dst = obj + lay->obj_offset[l] + j * lay->stride[l] % 64;"),
+    "block_table_index_transposed": (
+        "return ids[((int64_t)c * lay->n_kv_groups + g) * lay->k + j];",
+        "return ids[((int64_t)c * lay->k + j) * lay->n_kv_groups + g];"),
+    "smaller_kda_groups_first": (
+        "if (filled == base + (g < rem ? 1 : 0)) {",
+        "if (filled == base + (g >= m - rem ? 1 : 0)) {"),
+    "cover_rule_strict": (
+        "while (n * tok_bytes < kda_page)",
+        "while (n * tok_bytes <= kda_page)"),
+    "retrieve_writes_padding": (
+        "const uint8_t* src = obj + lay->obj_offset[l] + j * lay->page[l];\n"
+        "                memcpy(dst, src, (size_t)lay->page[l]);",
+        "const uint8_t* src = obj + lay->obj_offset[l] + j * lay->page[l];\n"
+        "                memcpy(dst, src, (size_t)(lay->reserved[l] < lay->obj_bytes[lay->obj_group[l]]"
+        " - lay->obj_offset[l] - j * lay->page[l] ? lay->reserved[l] : lay->page[l]));"),
+    "object_groups_swapped": (
+        "lay->obj_group[l] = lay->is_mla[l] ? 1 : 0;",
+        "lay->obj_group[l] = lay->is_mla[l] ? 0 : 1;"),
+    "chunk_rounds_down": (
+        "    while (c < chunk_min)\n        c += n;",
+        "    while (c + n <= chunk_min)\n        c += n;"),
+    "stride_sums_groups": (
+        "            if (byte_offset > stride)\n                stride = byte_offset;",
+        "            stride += byte_offset;"),
+    "one_slab_too_few": (
+        "if (lay->index_in_group[l] + 1 > slabs)",
+        "if (lay->index_in_group[l] > slabs)"),
+    "last_block_of_chunk_skipped": (
+        "for (j = 0; j < lay->k; j++) {\n"
+        "                int64_t id = block_id(lay, block_ids, c, lay->kv_group[l], j);\n"
+        "                const uint8_t* src",
+        "for (j = 0; j < lay->k - (lay->k > 1); j++) {\n"
+        "                int64_t id = block_id(lay, block_ids, c, lay->kv_group[l], j);\n"
+        "                const uint8_t* src"),
+    "conv_state_keeps_kernel_columns": (
+        "int64_t conv = (int64_t)conv_dim * (conv_kernel - 1) * conv_bytes;",
+        "int64_t conv = (int64_t)conv_dim * conv_kernel * conv_bytes;"),
+}
+
+
+def pin_checks():
+    """The pins, cheapest first (the property test last)."""
+    out = []
+    for row in golden_io.rows("block_sizes.txt"):
+        out.append(lambda r=row: pins.test_unified_block_size_matches_pages(r))
+    out += [pins.test_block_size_cover_is_inclusive, pins.test_tiny_block_size_and_tp_scaling,
+            pins.test_state_dtype_reading_is_the_only_one_matching_both_pages]
+    for row in golden_io.rows("chunk_negotiation.txt"):
+        out.append(lambda r=row: pins.test_chunk_negotiation(r))
+    out.append(pins.test_chunk_is_smallest_multiple)
+    for row in golden_io.rows("batch_budget.txt"):
+        out.append(lambda r=row: pins.test_batch_budget(r))
+    out += [pins.test_k3_groups_and_slabs_match_flat_kv,
+            pins.test_groups_hold_one_layer_type_and_are_contiguous,
+            pins.test_config_closed_forms]
+    for name in ("tiny", "kl_tp2", "kl_tp1", "k3_tp8", "long_ctx"):
+        out.append(lambda n=name: pins.test_config_layouts_structure(n))
+    out.append(pins.test_mla_object_is_chunk_tokens_by_latent_array)
+    for case in pins.BRUTE:
+        out.append(lambda c=case: pins.test_brute_force_every_injective_assignment(c))
+    out += [pins.test_id_range_and_alias_errors, pins.test_random_layouts_store_retrieve_properties]
+    return out
+
+
+def run_pins_against(lib_path: str) -> int:
+    """Runs the pins against the oracle build at lib_path; returns 1 if one
+    fails, 0 if all pass (used in a child process)."""
+    oracle._lib = oracle.bind(ctypes.CDLL(lib_path))
+    for check in pin_checks():
+        try:
+            check()
+        except (AssertionError, oracle.OracleError):
+            return 1
+    return 0
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    original, planted = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(original) == 1, "the mutation site moved; update the test"
+    mutant = tmp_path / "hkvref.c"
+    mutant.write_text(src.replace(original, planted))
+    (tmp_path / "hkvref.h").write_text(open(SRC[:-1] + "h").read())
+    so = tmp_path / "libmut.so"
+    subprocess.run(["gcc", "-O1", "-w", "-fPIC", "-shared", str(mutant), "-o", str(so)],
+                   check=True)
+    # a child process: a mutant may also crash (e.g. divide by zero), which
+    # counts as caught
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; from tests.test_oracle_mutations import run_pins_against; "
+            f"sys.exit(10 + run_pins_against({str(so)!r}))")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                       timeout=600)
+    assert r.returncode != 10, f"no pin fails with the planted mistake '{name}'"
+    assert r.returncode == 11 or r.returncode < 0 or r.returncode > 11, r.stderr[-2000:]
