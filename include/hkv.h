@@ -109,7 +109,7 @@ typedef struct hkv_layout_desc {
                                  object groups are separated (HKV_E_BATCH) ("Kimi-Linear"
                                  recipe, Why these settings; "Hybrid Attention Models",
                                  Step 2) */
-  uint64_t tile_bytes;        /* 0 = default (256 KiB); else the largest span one
+  uint64_t tile_bytes;        /* 0 = default (4 KiB); else the largest span one
                                  workgroup copies: a multiple of 4096 up to 1 GiB.  A
                                  tuning knob: results do not depend on it */
   uint32_t max_workgroups;    /* 0 = one workgroup per tile; else the grid is capped at

@@ -68,11 +68,25 @@ class hkv_chunk_batch(ctypes.Structure):
                 ("objects", ctypes.POINTER(vp))]
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+def one_hip_runtime() -> None:
+    """A process must hold one HIP runtime.  PyTorch-ROCm ships its own copy,
+    which its libraries load by file name; if libhkv.so were loaded first it
+    would bring the system runtime and torch would then load a second one
+    (each sees the GPU alone, and device memory of one is not usable from the
+    other).  Importing torch first makes libhkv bind to torch's runtime."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+
+
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads a build of libhkv and declares its signatures."""
+    one_hip_runtime()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built: run __graft_entry__.build() "
                           "(hipcc --offload-arch=gfx950); there is no fallback")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     L.hkv_unified_block_size.restype = i32
     L.hkv_unified_block_size.argtypes = [ctypes.POINTER(hkv_model), i32, ctypes.POINTER(i64)]
     L.hkv_layout_init.restype = i32
@@ -233,14 +247,15 @@ class Layout:
     """Owns a layout handle; exposes its summary and per-layer placements."""
 
     def __init__(self, desc: dict):
+        self._lib = lib  # the build that owns the handle
         self.handle = hkv_layout_init(desc)
         self.info = hkv_layout_info_get(self.handle)
         self.layers = [hkv_layer_info_get(self.handle, l) for l in range(self.info["n_layers"])]
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h:
-            hkv_layout_destroy(h)
+        if h and getattr(self, "_lib", None) is not None:
+            self._lib.hkv_layout_destroy(h)
             self.handle = None
 
     @property

@@ -217,8 +217,12 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   a.n_kv_groups = (uint32_t)G;
   a.blocks_per_chunk = (uint32_t)k;
   a.n_obj_groups = (uint32_t)O;
+  // One workgroup per tile, unless capped by the caller or by the 32-bit
+  // grid size (workgroups x threads); workgroups then loop over tiles.
   uint64_t grid = a.total_items;
   if (p.max_workgroups && grid > p.max_workgroups) grid = p.max_workgroups;
+  const uint64_t grid_limit = 0xFFFFFFFFull / hkv::kCopyThreads;
+  if (grid > grid_limit) grid = grid_limit;
   const int e = hkv::launch_copy(store, a, (uint32_t)grid, stream);
   if (e != 0) return hip_error((hipError_t)e, store ? "launching hkv_store_gather"
                                                     : "launching hkv_retrieve_scatter");

@@ -7,7 +7,10 @@
 
 namespace hkv {
 
-constexpr uint32_t kCopyThreads = 256;
+#ifndef HKV_THREADS
+#define HKV_THREADS 128  // two waves per workgroup
+#endif
+constexpr uint32_t kCopyThreads = HKV_THREADS;
 
 // Enqueues the gather (store) or scatter (retrieve) kernel over
 // a.total_items work items with `grid` workgroups on `stream` (a

@@ -23,7 +23,7 @@ namespace hkv {
 namespace {
 
 constexpr int64_t kAlignTokens = 16;
-constexpr uint64_t kDefaultTile = 256u << 10;
+constexpr uint64_t kDefaultTile = 4096;  // measured best on MI355X for both directions
 constexpr uint64_t kMaxTile = 1ull << 30;
 
 bool mul_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_mul_overflow(a, b, r); }

@@ -174,3 +174,17 @@ def test_call_validation_on_host():
     assert hkv.status_of(hkv.hkv_store_chunks, 0, pool, ids, objs, ws, ws_bytes, 0) \
         == hkv.HKV_E_ARG
     assert "workspace" in hkv.hkv_last_error() or hkv.hkv_last_error() != ""
+
+
+def test_one_hip_runtime_in_the_process():
+    """libhkv must bind to the HIP runtime torch uses: two runtimes in one
+    process each see the GPU alone (the second reports no device)."""
+    import re
+    import torch  # noqa: F401
+    import workloads
+    workloads._load_fill()
+    maps = open("/proc/self/maps").read()
+    hip = set(re.findall(r"\S*libamdhip64\S*", maps))
+    hsa = set(re.findall(r"\S*libhsa-runtime64\S*", maps))
+    assert len(hip) == 1, hip
+    assert len(hsa) == 1, hsa

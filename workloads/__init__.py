@@ -119,6 +119,7 @@ def _load_fill():
     if _fill_lib is None:
         if not os.path.exists(FILL_LIB_PATH):
             raise RuntimeError(f"{FILL_LIB_PATH} is not built; run __graft_entry__.build()")
+        import torch  # noqa: F401  (bind to torch's HIP runtime; see retrieve_store_chunk_amd)
         L = ctypes.CDLL(FILL_LIB_PATH)
         L.hkvfill_splitmix.restype = ctypes.c_int
         L.hkvfill_splitmix.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,

@@ -39,19 +39,28 @@ extern "C" int hkvfill_splitmix(void* dst, uint64_t nbytes, uint64_t seed, uint6
                                 void* stream) {
   if (nbytes == 0) return 0;
   if (reinterpret_cast<uintptr_t>(dst) & 7) return (int)hipErrorInvalidValue;
+  // The launch statuses are returned directly: hipGetLastError() would also
+  // report an earlier failure of any other HIP call on this thread.
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const uint64_t n_words = nbytes / 8;
   const uint32_t n_tail = (uint32_t)(nbytes % 8);
   if (n_words) {
     uint64_t blocks = (n_words + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(splitmix_fill_words, dim3((uint32_t)blocks), dim3(256), 0, s,
-                       reinterpret_cast<uint64_t*>(dst), n_words, seed, word0);
+    uint64_t* words = reinterpret_cast<uint64_t*>(dst);
+    void* args[] = {&words, const_cast<uint64_t*>(&n_words), &seed, &word0};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&splitmix_fill_words),
+                                         dim3((uint32_t)blocks), dim3(256), args, 0, s);
+    if (e != hipSuccess) return (int)e;
   }
   if (n_tail) {
-    hipLaunchKernelGGL(splitmix_fill_tail, dim3(1), dim3(64), 0, s,
-                       reinterpret_cast<uint8_t*>(dst) + n_words * 8, n_tail, seed,
-                       word0 + n_words);
+    uint8_t* tail = reinterpret_cast<uint8_t*>(dst) + n_words * 8;
+    uint64_t q = word0 + n_words;
+    uint32_t nt = n_tail;
+    void* args[] = {&tail, &nt, &seed, &q};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&splitmix_fill_tail),
+                                         dim3(1), dim3(64), args, 0, s);
+    if (e != hipSuccess) return (int)e;
   }
-  return (int)hipGetLastError();
+  return 0;
 }
