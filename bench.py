@@ -90,6 +90,44 @@ def cpu_baseline(cfg, min_seconds: float = 10.0, max_seconds: float = 30.0) -> d
                       "single-threaded plain C memcpy"}
 
 
+def hbm_ceiling(buf, stream, reps: int = 10) -> dict:
+    """Pure read, pure write and contiguous copy of 16 GiB halves of `buf`
+    with kernels shaped like the library's (workloads/hbm_ceiling.hip)."""
+    import ctypes
+
+    import torch
+    import workloads as W
+    L = ctypes.CDLL(os.path.join(os.path.dirname(W.__file__), "libhkvceiling.so"))
+    L.hkvceiling_launch.restype = ctypes.c_int
+    L.hkvceiling_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    n = min(16 << 30, (buf.numel() // 2) // 4096 * 4096)
+    if n < (1 << 30):
+        return {"skipped": "needs a pool of at least 2 GiB"}
+    src, dst = buf[:n], buf[n:2 * n]
+    out = torch.empty(n // 4096 * 4, dtype=torch.uint8, device=buf.device)
+    res = {"bytes": n}
+    for kind, name, traffic in ((0, "read", n), (1, "write", n), (2, "copy", 2 * n)):
+        def launch():
+            rc = L.hkvceiling_launch(kind, src.data_ptr(), dst.data_ptr(), out.data_ptr(), n,
+                                     stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"hbm ceiling launch failed: HIP error {rc}")
+        launch()
+        launch()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            launch()
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name + "_GBs"] = round(traffic / (ms / 1e3) / 1e9, 1)
+    res["what"] = ("4 KiB tile per 128-thread workgroup, XCD order, 16-byte nontemporal "
+                   "accesses; copy = one contiguous buffer into another")
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,7 +139,11 @@ def main() -> int:
     ap.add_argument("--max-workgroups", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ceiling", action="store_true",
-                    help="also time a plain device-to-device copy of the same bytes")
+                    help="also time torch copy_ of one 8 GiB buffer (a plain copy kernel of "
+                         "known size, used to calibrate the rocprofv3 byte counters)")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="also time pure-read, pure-write and contiguous-copy kernels built "
+                         "like the library's (HBM reference rates)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -226,6 +268,10 @@ def main() -> int:
                                "hbm_GBs": round(2 * n / (ms / 1e3) / 1e9, 1),
                                "what": "torch copy_ of one contiguous buffer (read + write)"}
         log(f"copy ceiling: {out['copy_ceiling']['hbm_GBs']} GB/s")
+
+    if args.hbm_ceiling:
+        out["hbm_ceiling"] = hbm_ceiling(g.pool, stream)
+        log(f"HBM reference rates: {out['hbm_ceiling']}")
 
     del g
     torch.cuda.empty_cache()
