@@ -21,6 +21,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+HOST_LINK_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction (32 GT/s x 16 lanes, 128b/130b)
 METRIC = "store+retrieve GB/s of KV/state pages (Kimi-Linear shapes, N=1888); % HBM peak"
 COPY_SRC = os.path.join(ROOT, "retrieve_store_chunk_amd", "csrc", "hkv_copy.hip")
 
@@ -128,19 +129,45 @@ def hbm_ceiling(buf, stream, reps: int = 10) -> dict:
     return res
 
 
+def host_link_ceiling(stream, reps: int = 3) -> dict:
+    """DMA copies of 4 GiB between pinned host memory and HBM (torch copy_)."""
+    import torch
+    n = 4 << 30
+    dev = torch.empty(n, dtype=torch.uint8, device="cuda")
+    host = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    res = {"bytes": n}
+    with torch.cuda.stream(stream):
+        for name, fn in (("device_to_host", lambda: host.copy_(dev, non_blocking=True)),
+                         ("host_to_device", lambda: dev.copy_(host, non_blocking=True))):
+            fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            e1.synchronize()
+            res[name + "_GBs"] = round(n / (e0.elapsed_time(e1) / reps / 1e3) / 1e9, 1)
+    del dev, host
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="kl_tp1",
-                    help="workload: tiny, kl_tp2, kl_tp1 (default), k3_tp8, long_ctx")
+                    help="workload: tiny, kl_tp2, kl_tp1 (default), k3_tp8, long_ctx, "
+                         "kl_tp1_host (objects in pinned host memory)")
     ap.add_argument("--tile-bytes", type=int, default=0)
     ap.add_argument("--max-workgroups", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ceiling", action="store_true",
                     help="also time torch copy_ of one 8 GiB buffer (a plain copy kernel of "
                          "known size, used to calibrate the rocprofv3 byte counters)")
+    ap.add_argument("--host-link-ceiling", action="store_true",
+                    help="also time 4 GiB DMA copies between pinned host memory and HBM "
+                         "(host-link reference rates)")
     ap.add_argument("--hbm-ceiling", action="store_true",
                     help="also time pure-read, pure-write and contiguous-copy kernels built "
                          "like the library's (HBM reference rates)")
@@ -160,7 +187,9 @@ def main() -> int:
         return 1
     cfg = W.make_config(args.config)
     log(f"workload {cfg.name}: {cfg.title}")
-    g = GpuWorkload(cfg, tile_bytes=args.tile_bytes, max_workgroups=args.max_workgroups)
+    objects_on = cfg.extra.get("objects", "device")
+    g = GpuWorkload(cfg, tile_bytes=args.tile_bytes, max_workgroups=args.max_workgroups,
+                    objects=objects_on)
     info = g.info
     log(f"layout: N={info['block_size']} C={info['chunk_tokens']} k={info['blocks_per_chunk']} "
         f"blocks={info['num_blocks']} stride={info['block_stride']} "
@@ -210,21 +239,39 @@ def main() -> int:
         k["launches"] += args.steps
         k["ms"] += sum(ms)
         k["payload"] += per_wave_payload[i] * args.steps
+    # Device objects: every page byte is read from and written to HBM, so the
+    # traffic is 2 x payload against the HBM peak.  Host objects: the object
+    # side crosses the host link once per byte, so payload against the link.
+    on_host = objects_on == "host"
     kernels = {}
     for name, k in kern.items():
         avg_ms = k["ms"] / k["launches"]
-        bytes_per_launch = 2 * k["payload"] / k["launches"]  # read + write of every page
-        kernels[name] = {"launches_per_step": k["launches"] // args.steps,
-                         "avg_ms": round(avg_ms, 4),
-                         "hbm_bytes_per_launch": int(bytes_per_launch),
-                         "hbm_GBs": round(bytes_per_launch / (avg_ms / 1e3) / 1e9, 1)}
-    dom = max(kernels, key=lambda n: kernels[n]["hbm_bytes_per_launch"] *
-              kernels[n]["launches_per_step"])
-    achieved = kernels[dom]["hbm_GBs"]
-    traffic = load_traffic(args.config, args.tile_bytes, args.max_workgroups) \
-        if dom == "hkv_store_gather" else None
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+        if on_host:
+            link = k["payload"] / k["launches"]
+            kernels[name] = {"launches_per_step": k["launches"] // args.steps,
+                             "avg_ms": round(avg_ms, 4),
+                             "link_bytes_per_launch": int(link),
+                             "link_GBs": round(link / (avg_ms / 1e3) / 1e9, 2)}
+        else:
+            hbm = 2 * k["payload"] / k["launches"]  # read + write of every page
+            kernels[name] = {"launches_per_step": k["launches"] // args.steps,
+                             "avg_ms": round(avg_ms, 4),
+                             "hbm_bytes_per_launch": int(hbm),
+                             "hbm_GBs": round(hbm / (avg_ms / 1e3) / 1e9, 1)}
+    unit_key = "link_bytes_per_launch" if on_host else "hbm_bytes_per_launch"
+    dom = max(kernels, key=lambda n: kernels[n][unit_key] * kernels[n]["launches_per_step"])
+    if on_host:
+        achieved = kernels[dom]["link_GBs"]
+        roofline = {"bound": "host-link", "kernel": dom, "achieved": achieved,
+                    "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HOST_LINK_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = kernels[dom]["hbm_GBs"]
+        traffic = load_traffic(args.config, args.tile_bytes, args.max_workgroups) \
+            if dom == "hkv_store_gather" else None
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic}
 
     out = {
         "metric": METRIC,
@@ -245,7 +292,9 @@ def main() -> int:
                    "block_size": info["block_size"], "chunk_tokens": info["chunk_tokens"],
                    "path": "B packed" if info["path"] else "A padded-unified",
                    "tile_bytes": args.tile_bytes, "max_workgroups": args.max_workgroups},
-        "pct_hbm_peak": round(100 * 2 * value / HBM_PEAK_GBS, 2),
+        "objects": objects_on,
+        "pct_hbm_peak": None if on_host else round(100 * 2 * value / HBM_PEAK_GBS, 2),
+        "pct_host_link_peak": round(100 * value / HOST_LINK_PEAK_GBS, 2) if on_host else None,
         "chunks_per_s": round(sum(len(w.chunks) for w in g.waves) / (ms_per_step / 1e3), 1),
         "kernels": kernels,
         "roofline": roofline,
@@ -268,6 +317,10 @@ def main() -> int:
                                "hbm_GBs": round(2 * n / (ms / 1e3) / 1e9, 1),
                                "what": "torch copy_ of one contiguous buffer (read + write)"}
         log(f"copy ceiling: {out['copy_ceiling']['hbm_GBs']} GB/s")
+
+    if args.host_link_ceiling:
+        out["host_link_ceiling"] = host_link_ceiling(stream)
+        log(f"host link reference rates: {out['host_link_ceiling']}")
 
     if args.hbm_ceiling:
         out["hbm_ceiling"] = hbm_ceiling(g.pool, stream)

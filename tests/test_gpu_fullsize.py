@@ -44,12 +44,12 @@ def _samples(rng, w, n_layers, k, count):
     return sorted(out)
 
 
-@pytest.mark.parametrize("name", W.CONFIG_NAMES)
+@pytest.mark.parametrize("name", W.CONFIG_NAMES + W.EXTRA_CONFIG_NAMES)
 def test_full_size_sampled(name):
     from workloads.driver import GpuWorkload
     cfg = W.make_config(name)
     print(f"[fullsize] {name}", flush=True)
-    g = GpuWorkload(cfg)
+    g = GpuWorkload(cfg, objects=cfg.extra.get("objects", "device"))
     ref = oracle.Layout(cfg.desc)
     assert g.info["num_blocks"] == ref.summary["num_blocks"]
     assert g.info["pool_bytes_used"] == ref.summary["pool_bytes_used"]

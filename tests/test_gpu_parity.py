@@ -29,10 +29,10 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-def run_parity(cfg, tile_bytes=0, max_workgroups=0, pool_fill=None):
+def run_parity(cfg, tile_bytes=0, max_workgroups=0, pool_fill=None, objects="device"):
     from workloads.driver import GpuWorkload
-    _log(f"[parity] {cfg.name} tile={tile_bytes} max_wg={max_workgroups}")
-    g = GpuWorkload(cfg, tile_bytes=tile_bytes, max_workgroups=max_workgroups)
+    _log(f"[parity] {cfg.name} tile={tile_bytes} max_wg={max_workgroups} objects={objects}")
+    g = GpuWorkload(cfg, tile_bytes=tile_bytes, max_workgroups=max_workgroups, objects=objects)
     ref = oracle.Layout(cfg.desc)
     for key, okey in (("num_blocks", "num_blocks"), ("pool_bytes_used", "pool_bytes_used"),
                       ("n_kv_groups", "n_kv_groups"), ("blocks_per_chunk", "blocks_per_chunk")):
@@ -151,6 +151,18 @@ EDGE = [
 def test_edge_layouts(cfg):
     run_parity(cfg)
     run_parity(cfg, tile_bytes=4096, max_workgroups=3)
+
+
+@pytest.mark.parametrize("name", ["tiny", "kl_tp1_host", "k3_tp8", "long_ctx"])
+def test_host_object_parity(name):
+    """Chunk objects in pinned host memory (the GPU reads and writes them over
+    the host link): the same bytes as the oracle."""
+    run_parity(W.make_small_config(name), objects="host")
+
+
+@pytest.mark.parametrize("cfg", [EDGE[0], EDGE[2]], ids=lambda c: c.name)
+def test_host_object_parity_edge_layouts(cfg):
+    run_parity(cfg, objects="host")
 
 
 def test_empty_batch_is_a_noop():

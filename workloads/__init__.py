@@ -250,10 +250,23 @@ def make_config(name: str) -> Config:
                       seed, shared_permutation=True,
                       notes="a 1,000,000-token prefix is 530 whole chunks of 1888 tokens; each "
                             "2k-token request has one whole chunk")
+    if name == "kl_tp1_host":
+        seed = 0x48B0006
+        req = [8] * 16
+        desc = _desc(KIMI_LINEAR_27, 32, 128, 12288, 2, 1, 64 * GIB)
+        return Config(name, "Kimi-Linear full state (TP=1), path B, chunk objects in pinned "
+                      "host memory", desc, req,
+                      [Phase("store", _all_chunks(req)),
+                       Phase("retrieve", _all_chunks(req, first=4))], seed,
+                      notes="16 requests x 8 chunks stored to host objects (7.5 GB pinned), "
+                            "the first 4 chunks of each retrieved from them",
+                      extra={"objects": "host"})
     raise KeyError(name)
 
 
 CONFIG_NAMES = ("tiny", "kl_tp2", "kl_tp1", "k3_tp8", "long_ctx")
+# Further workloads beyond the five above.
+EXTRA_CONFIG_NAMES = ("kl_tp1_host",)
 
 
 def make_small_config(name: str) -> Config:
@@ -278,6 +291,11 @@ def make_small_config(name: str) -> Config:
         cfg.requests = [2] * 7
         cfg.phases = [Phase("store", _all_chunks(cfg.requests)),
                       Phase("retrieve", _all_chunks(cfg.requests))]
+    elif name == "kl_tp1_host":
+        cfg.desc["pool_bytes"] = 1 * GIB
+        cfg.requests = [4] * 3
+        cfg.phases = [Phase("store", _all_chunks(cfg.requests)),
+                      Phase("retrieve", _all_chunks(cfg.requests, first=2))]
     elif name == "long_ctx":
         cfg.desc["pool_bytes"] = 1 * GIB
         cfg.requests = [8] + [1] * 8

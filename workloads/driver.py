@@ -19,8 +19,14 @@ def _align(x: int, a: int = 256) -> int:
 
 class GpuWorkload:
     def __init__(self, cfg: W.Config, device: str = "cuda:0", tile_bytes: int = 0,
-                 max_workgroups: int = 0, stream: torch.cuda.Stream | None = None):
+                 max_workgroups: int = 0, stream: torch.cuda.Stream | None = None,
+                 objects: str = "device"):
+        """objects: "device" (HBM) or "host" (pinned host memory, which the
+        GPU reads and writes over the host link)."""
+        if objects not in ("device", "host"):
+            raise ValueError("objects must be 'device' or 'host'")
         self.cfg = cfg
+        self.objects_on = objects
         self.device = torch.device(device)
         desc = dict(cfg.desc, tile_bytes=tile_bytes, max_workgroups=max_workgroups)
         self.layout = hkv.Layout(desc)
@@ -37,8 +43,12 @@ class GpuWorkload:
         self.obj_stride = [_align(max(1, info["obj_bytes"][o])) for o in range(self.layout.O)]
         self.pool = torch.empty(_align(info["pool_bytes_used"]), dtype=torch.uint8,
                                 device=self.device)
-        self.objs = [torch.empty(n_slots * self.obj_stride[o], dtype=torch.uint8,
-                                 device=self.device) for o in range(self.layout.O)]
+        if objects == "device":
+            self.objs = [torch.empty(n_slots * self.obj_stride[o], dtype=torch.uint8,
+                                     device=self.device) for o in range(self.layout.O)]
+        else:
+            self.objs = [torch.empty(n_slots * self.obj_stride[o], dtype=torch.uint8,
+                                     pin_memory=True) for o in range(self.layout.O)]
         max_chunks = max((len(w.chunks) for w in self.waves), default=0)
         self.ws_bytes = self.layout.workspace_size(max_chunks)
         self.ws = torch.empty(max(256, self.ws_bytes), dtype=torch.uint8, device=self.device)
@@ -66,10 +76,16 @@ class GpuWorkload:
                        self.stream.cuda_stream)
 
     def fill_objects(self, seed: int) -> None:
-        with torch.cuda.stream(self.stream):
-            for o in range(self.layout.O):
+        """Every object byte: group o's buffer is the stream derive_seed(seed, o)
+        (filled by the GPU in device memory, by the host in pinned memory)."""
+        for o in range(self.layout.O):
+            if self.objects_on == "device":
                 W.gpu_fill(self.objs[o].data_ptr(), self.objs[o].numel(),
                            W.derive_seed(seed, o), 0, self.stream.cuda_stream)
+            else:
+                self.stream.synchronize()
+                self.objs[o].numpy()[:] = W.fill_bytes(W.derive_seed(seed, o), 0,
+                                                       self.objs[o].numel())
 
     def prefill_objects(self) -> None:
         """Objects that a retrieve reads without an earlier store in this run
@@ -80,9 +96,12 @@ class GpuWorkload:
                 for rc in w.chunks:
                     for o in range(self.layout.O):
                         v = self.object_view(rc, o)
-                        W.gpu_fill(v.data_ptr(), v.numel(),
-                                   W.derive_seed(W.object_seed(self.cfg, *rc), o), 0,
-                                   self.stream.cuda_stream)
+                        seed = W.derive_seed(W.object_seed(self.cfg, *rc), o)
+                        if self.objects_on == "device":
+                            W.gpu_fill(v.data_ptr(), v.numel(), seed, 0, self.stream.cuda_stream)
+                        else:
+                            self.stream.synchronize()
+                            v.numpy()[:] = W.fill_bytes(seed, 0, v.numel())
 
     # ------------------------------------------------------------ calls
     def run_wave(self, w: W.Wave) -> None:
@@ -127,4 +146,4 @@ class GpuWorkload:
 
     def host_object(self, rc, o) -> np.ndarray:
         self.stream.synchronize()
-        return self.object_view(rc, o).cpu().numpy()
+        return self.object_view(rc, o).cpu().numpy().copy()
