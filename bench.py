@@ -151,6 +151,26 @@ def host_link_ceiling(stream, reps: int = 3) -> dict:
     return res
 
 
+def chunk_keys_timing(g, cfg, tokens_per_request: int = 16384) -> dict:
+    """Host time of hkv_chunk_keys for every request of the step: seeded
+    synthetic token ids, one call per request, hash blocks of N tokens."""
+    import numpy as np
+    import workloads as W
+    n_req = len(cfg.requests)
+    rng = np.random.default_rng(W.derive_seed(cfg.seed, 31337) % (1 << 32))
+    toks = rng.integers(0, 163840, (n_req, tokens_per_request), dtype=np.int64).astype(np.int32)
+    g.layout.chunk_keys(toks[0])  # warm
+    t0 = time.perf_counter()
+    n_keys = 0
+    for r in range(n_req):
+        _, keys = g.layout.chunk_keys(toks[r], rank_tag=(1 << 32) | 0)
+        n_keys += keys.size
+    dt = time.perf_counter() - t0
+    return {"requests": n_req, "tokens": int(toks.size), "keys": n_keys,
+            "ms": round(dt * 1e3, 3), "Mtokens_per_s": round(toks.size / dt / 1e6, 1),
+            "what": "host, one thread, one call per request (hash blocks of N tokens)"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,6 +337,9 @@ def main() -> int:
                                "hbm_GBs": round(2 * n / (ms / 1e3) / 1e9, 1),
                                "what": "torch copy_ of one contiguous buffer (read + write)"}
         log(f"copy ceiling: {out['copy_ceiling']['hbm_GBs']} GB/s")
+
+    out["chunk_keys"] = chunk_keys_timing(g, cfg)
+    log(f"chunk keys: {out['chunk_keys']}")
 
     if args.host_link_ceiling:
         out["host_link_ceiling"] = host_link_ceiling(stream)

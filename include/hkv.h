@@ -216,6 +216,60 @@ hkv_status hkv_retrieve_chunks(const hkv_layout* layout, void* pool,
                                const hkv_chunk_batch* batch, void* workspace,
                                size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Object identity.  Cached pages are byte-opaque, so an entry must never be
+ * read back by an engine whose object format differs: other attention
+ * backends or kernel block sizes ("Kimi-Linear", "Kimi K3" recipes and
+ * "Hybrid Attention Models", Caveats).  Objects are told apart by cache
+ * group, prefix hash and parallel configuration (Mooncake K3 blog, vLLM x
+ * Mooncake: hybrid cache reuse across instances).
+ *
+ * All hashing uses mix64, the output function of SplitMix64 (Steele, Lea and
+ * Flood, OOPSLA 2014):
+ *   mix64(z): z ^= z >> 30; z *= 0xBF58476D1CE4E5B9; z ^= z >> 27;
+ *             z *= 0x94D049BB133111EB; z ^= z >> 31.
+ * and GAMMA = 0x9E3779B97F4A7C15.  All arithmetic is modulo 2^64.
+ * ------------------------------------------------------------------------ */
+
+/* 64-bit fingerprint of the chunk-object format: it changes whenever the
+ * bytes of an object would mean something else, and only then.  It folds,
+ * with f = mix64(f ^ w) from f = GAMMA, the words: 1 (format version), N,
+ * k, n_layers, kda_heads, kda_head_dim, kda_state_bytes, conv_dim,
+ * conv_kernel, conv_bytes, mla_width, mla_bytes, n_obj_groups, and per layer
+ * in model order is_mla | obj_group << 1 | page_bytes << 8.  The pool path,
+ * pool size, KV grouping and tuning knobs do not enter it: they do not change
+ * object bytes, so objects stored from a path A pool can be retrieved into a
+ * path B pool of the same model.  Errors: HKV_E_ARG. */
+hkv_status hkv_layout_fingerprint(const hkv_layout* layout, uint64_t* out);
+
+/* Chained prefix hashes and object keys for one request (vLLM hybrid
+ * KV-cache blog, section 6.3: hashes are computed per hash block and each
+ * folds in the previous one, so the i-th hash fingerprints the whole prefix;
+ * a coarse block's hash is the hash of its last fine sub-block).
+ *
+ *   tokens            HOST [n_tokens] token ids of the request, in order;
+ *   hash_block_tokens h: a divisor of N (0 = N);
+ *   root              H_0, e.g. 0 or the hash a parent prefix ended on;
+ *   rank_tag          the caller's parallel configuration (e.g. tp_size << 32
+ *                     | tp_rank), mixed into every key;
+ *   prefix_hashes_out HOST [n_tokens / h] or NULL: H_1 .. H_(n_tokens/h);
+ *   keys_out          HOST [n_chunks][O] or NULL; n_chunks = n_tokens / C
+ *                     (whole chunks only; a trailing partial chunk has none),
+ *                     at most max_chunks are written;
+ *   n_chunks_out      the number of whole chunks (may exceed max_chunks).
+ *
+ * Definitions (t_j = tokens[(i-1)*h + j], j = 0..h-1, as uint32):
+ *   content_i = fold of c = mix64(c ^ (t_j | j << 32)) over j from c = GAMMA
+ *   H_i       = mix64((H_{i-1} ^ content_i) + GAMMA)
+ *   prefix(c) = H_{(c+1) C / h}                       (the chunk's last fine block)
+ *   key(c, o) = mix64(mix64(fingerprint ^ rank_tag) ^ (prefix(c) + (o+1) GAMMA))
+ * Errors: HKV_E_ARG (NULL tokens with n_tokens > 0, h not dividing N,
+ * negative counts). */
+hkv_status hkv_chunk_keys(const hkv_layout* layout, const int32_t* tokens, int64_t n_tokens,
+                          int32_t hash_block_tokens, uint64_t root, uint64_t rank_tag,
+                          uint64_t* prefix_hashes_out, uint64_t* keys_out, int32_t max_chunks,
+                          int64_t* n_chunks_out);
+
 /* Message for the calling thread's last non-OK status ("" if none).  The
  * pointer stays valid until the thread's next hkv_* call. */
 const char* hkv_last_error(void);

@@ -70,6 +70,11 @@ def bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.hkvref_store_chunks.argtypes = [vp, vp, i32, vp, vp]
     L.hkvref_retrieve_chunks.restype = ctypes.c_int
     L.hkvref_retrieve_chunks.argtypes = [vp, vp, i32, vp, vp]
+    L.hkvref_fingerprint.restype = u64
+    L.hkvref_fingerprint.argtypes = [vp]
+    L.hkvref_chunk_keys.restype = ctypes.c_int
+    L.hkvref_chunk_keys.argtypes = [vp, vp, i64, i32, u64, u64, vp, vp, i32,
+                                    ctypes.POINTER(i64)]
     return L
 
 
@@ -204,3 +209,23 @@ class Layout:
         rc = self._L.hkvref_retrieve_chunks(self._h, pool.ctypes.data, n, ids.ctypes.data, addrs)
         if rc != OK:
             raise OracleError(rc, "retrieve_chunks")
+
+    def fingerprint(self) -> int:
+        return int(self._L.hkvref_fingerprint(self._h))
+
+    def chunk_keys(self, tokens, hash_block_tokens=0, root=0, rank_tag=0):
+        """(prefix hashes [n_tokens // h], keys [n_chunks][O]) as uint64 arrays."""
+        toks = np.ascontiguousarray(tokens, dtype=np.int32)
+        h = hash_block_tokens or self.summary["block_size"]
+        n_fine = toks.size // h if h > 0 else 0
+        n_chunks = toks.size // self.summary["chunk_tokens"]
+        prefix = np.zeros(max(1, n_fine), dtype=np.uint64)
+        keys = np.zeros((max(1, n_chunks), self.O), dtype=np.uint64)
+        got = ctypes.c_int64()
+        rc = self._L.hkvref_chunk_keys(self._h, toks.ctypes.data, toks.size, hash_block_tokens,
+                                       root & (2**64 - 1), rank_tag & (2**64 - 1),
+                                       prefix.ctypes.data, keys.ctypes.data, n_chunks,
+                                       ctypes.byref(got))
+        if rc != OK:
+            raise OracleError(rc, "chunk_keys")
+        return prefix[:n_fine], keys[:got.value]

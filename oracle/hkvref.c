@@ -19,6 +19,8 @@ struct hkvref_layout {
     int64_t block_stride;  /* path B (path A: = unified_page) */
     int64_t addressed_bytes;
     int64_t obj_bytes[2];
+    int64_t shape[8]; /* heads, head_dim, state_bytes, conv_dim, conv_kernel, conv_bytes,
+                         mla_width, mla_bytes */
     int32_t* is_mla;
     int32_t* kv_group;
     int32_t* obj_group;
@@ -177,6 +179,14 @@ int hkvref_layout_init(int32_t n_layers, const uint8_t* is_mla_in,
         return HKVREF_E_ARG;
     lay->n_layers = n_layers;
     lay->path = path;
+    lay->shape[0] = heads;
+    lay->shape[1] = head_dim;
+    lay->shape[2] = state_bytes;
+    lay->shape[3] = conv_dim;
+    lay->shape[4] = conv_kernel;
+    lay->shape[5] = conv_bytes;
+    lay->shape[6] = mla_width;
+    lay->shape[7] = mla_bytes;
     lay->is_mla = (int32_t*)calloc((size_t)n_layers, sizeof(int32_t));
     lay->kv_group = (int32_t*)calloc((size_t)n_layers, sizeof(int32_t));
     lay->obj_group = (int32_t*)calloc((size_t)n_layers, sizeof(int32_t));
@@ -501,5 +511,93 @@ int hkvref_retrieve_chunks(const hkvref_layout* lay, uint8_t* pool,
             }
         }
     }
+    return HKVREF_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Object identity.  Cached pages are byte-opaque and must not be shared
+ * across engines whose object format differs (the recipes' and "Hybrid
+ * Attention Models"' Caveats); objects are told apart by cache group, prefix
+ * hash and parallel configuration (Mooncake K3 blog, vLLM x Mooncake).
+ * Hashes are chained per hash block, each folding in the previous one, and a
+ * coarse block takes its last fine sub-block's hash (vLLM hybrid KV-cache
+ * blog, section 6.3).  mix64 is SplitMix64's output function (Steele, Lea and
+ * Flood, OOPSLA 2014).
+ * ------------------------------------------------------------------------ */
+#define HKVREF_GAMMA 0x9E3779B97F4A7C15ULL
+
+static uint64_t ref_mix64(uint64_t z)
+{
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+
+uint64_t hkvref_fingerprint(const hkvref_layout* lay)
+{
+    uint64_t words[64];
+    uint64_t f = HKVREF_GAMMA;
+    int32_t i, l, n = 0;
+    words[n++] = 1;
+    words[n++] = (uint64_t)lay->n;
+    words[n++] = (uint64_t)lay->k;
+    words[n++] = (uint64_t)lay->n_layers;
+    for (i = 0; i < 8; i++)
+        words[n++] = (uint64_t)lay->shape[i];
+    words[n++] = (uint64_t)lay->n_obj_groups;
+    for (i = 0; i < n; i++)
+        f = ref_mix64(f ^ words[i]);
+    for (l = 0; l < lay->n_layers; l++) {
+        uint64_t w = (uint64_t)lay->is_mla[l] | ((uint64_t)lay->obj_group[l] << 1) |
+                     ((uint64_t)lay->page[l] << 8);
+        f = ref_mix64(f ^ w);
+    }
+    return f;
+}
+
+int hkvref_chunk_keys(const hkvref_layout* lay, const int32_t* tokens, int64_t n_tokens,
+                      int32_t hash_block, uint64_t root, uint64_t rank_tag,
+                      uint64_t* prefix_out, uint64_t* keys_out, int32_t max_chunks,
+                      int64_t* n_chunks_out)
+{
+    int64_t h = hash_block == 0 ? lay->n : hash_block;
+    int64_t n_fine, n_chunks, i, j, c;
+    uint64_t* H;
+    uint64_t base;
+    int32_t o;
+    if (n_tokens < 0 || max_chunks < 0 || n_chunks_out == NULL ||
+        (n_tokens > 0 && tokens == NULL))
+        return HKVREF_E_ARG;
+    if (h <= 0 || lay->n % h != 0)
+        return HKVREF_E_ARG;
+    n_fine = n_tokens / h;
+    n_chunks = n_tokens / lay->c;
+    /* H[0] = root; H[i] folds block i's content into H[i-1] */
+    H = (uint64_t*)malloc((size_t)(n_fine + 1) * sizeof(uint64_t));
+    if (H == NULL)
+        return HKVREF_E_ARG;
+    H[0] = root;
+    for (i = 1; i <= n_fine; i++) {
+        uint64_t content = HKVREF_GAMMA;
+        for (j = 0; j < h; j++) {
+            uint64_t t = (uint64_t)(uint32_t)tokens[(i - 1) * h + j];
+            content = ref_mix64(content ^ (t | ((uint64_t)j << 32)));
+        }
+        H[i] = ref_mix64((H[i - 1] ^ content) + HKVREF_GAMMA);
+        if (prefix_out != NULL)
+            prefix_out[i - 1] = H[i];
+    }
+    /* chunk c ends on fine block (c+1) * C / h */
+    base = ref_mix64(hkvref_fingerprint(lay) ^ rank_tag);
+    if (keys_out != NULL) {
+        for (c = 0; c < n_chunks && c < max_chunks; c++) {
+            uint64_t prefix = H[(c + 1) * lay->c / h];
+            for (o = 0; o < lay->n_obj_groups; o++)
+                keys_out[c * lay->n_obj_groups + o] =
+                    ref_mix64(base ^ (prefix + (uint64_t)(o + 1) * HKVREF_GAMMA));
+        }
+    }
+    free(H);
+    *n_chunks_out = n_chunks;
     return HKVREF_OK;
 }

@@ -95,4 +95,18 @@ int hkvref_retrieve_chunks(const hkvref_layout* lay, uint8_t* pool,
                            int32_t n_chunks, const int32_t* block_ids,
                            const uint8_t* const* objects);
 
+/* Object-format fingerprint: mix64-fold (f = mix64(f ^ w), f0 = GAMMA) of
+ * 1, N, k, n_layers, the eight per-rank shapes (heads, head_dim,
+ * state_bytes, conv_dim, conv_kernel, conv_bytes, mla_width, mla_bytes),
+ * n_obj_groups, then per layer is_mla | obj_group << 1 | page << 8. */
+uint64_t hkvref_fingerprint(const hkvref_layout* lay);
+
+/* Chained prefix hashes over hash blocks of h tokens (h divides N; 0 = N)
+ * and one key per (whole chunk, object group).  prefix_out [n_tokens / h]
+ * and keys_out [min(n_chunks, max_chunks)][O] may be NULL. */
+int hkvref_chunk_keys(const hkvref_layout* lay, const int32_t* tokens, int64_t n_tokens,
+                      int32_t hash_block, uint64_t root, uint64_t rank_tag,
+                      uint64_t* prefix_out, uint64_t* keys_out, int32_t max_chunks,
+                      int64_t* n_chunks_out);
+
 #endif

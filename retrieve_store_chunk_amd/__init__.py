@@ -105,6 +105,12 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.hkv_retrieve_chunks.restype = i32
     L.hkv_retrieve_chunks.argtypes = [vp, vp, ctypes.POINTER(hkv_chunk_batch), vp,
                                       ctypes.c_size_t, vp]
+    L.hkv_layout_fingerprint.restype = i32
+    L.hkv_layout_fingerprint.argtypes = [vp, ctypes.POINTER(u64)]
+    L.hkv_chunk_keys.restype = i32
+    L.hkv_chunk_keys.argtypes = [vp, ctypes.POINTER(i32), i64, i32, u64, u64,
+                                 ctypes.POINTER(u64), ctypes.POINTER(u64), i32,
+                                 ctypes.POINTER(i64)]
     L.hkv_last_error.restype = ctypes.c_char_p
     L.hkv_last_error.argtypes = []
     return L
@@ -196,7 +202,34 @@ def hkv_workspace_size(handle: int, max_chunks: int) -> int:
     return out.value
 
 
-def _batch(handle, block_ids, objects):
+def hkv_layout_fingerprint(handle: int) -> int:
+    out = u64()
+    _check(lib.hkv_layout_fingerprint(handle, ctypes.byref(out)), "hkv_layout_fingerprint")
+    return out.value
+
+
+def hkv_chunk_keys(handle: int, tokens, hash_block_tokens: int = 0, root: int = 0,
+                   rank_tag: int = 0, info: dict | None = None):
+    """Returns (prefix_hashes [n_tokens // h] uint64, keys [n_chunks][O] uint64).
+    `info` (the layout's hkv_layout_info_get) may be passed to skip the query."""
+    import numpy as np
+    toks = np.ascontiguousarray(tokens, dtype=np.int32)
+    info = info or hkv_layout_info_get(handle)
+    h = hash_block_tokens or info["block_size"]
+    n_fine = toks.size // h if h > 0 else 0
+    n_chunks = toks.size // info["chunk_tokens"]
+    prefix = np.zeros(max(1, n_fine), dtype=np.uint64)
+    keys = np.zeros((max(1, n_chunks), info["n_obj_groups"]), dtype=np.uint64)
+    got = i64()
+    p_u64 = ctypes.POINTER(u64)
+    _check(lib.hkv_chunk_keys(handle, toks.ctypes.data_as(ctypes.POINTER(i32)), toks.size,
+                              hash_block_tokens, root & (2**64 - 1), rank_tag & (2**64 - 1),
+                              prefix.ctypes.data_as(p_u64), keys.ctypes.data_as(p_u64),
+                              n_chunks, ctypes.byref(got)), "hkv_chunk_keys")
+    return prefix[:n_fine], keys[:got.value]
+
+
+def _batch(handle, block_ids, objects, info=None):
     """block_ids: int32 array [n][G][k]; objects: flat sequence of n*O device
     addresses (chunk-major).  Shapes are checked against the layout so the
     library never reads past the host arrays."""
@@ -204,7 +237,7 @@ def _batch(handle, block_ids, objects):
     ids = np.ascontiguousarray(block_ids, dtype=np.int32)
     n = int(ids.shape[0]) if ids.ndim else 0
     if handle:
-        info = hkv_layout_info_get(handle)
+        info = info or hkv_layout_info_get(handle)
         want = (n, info["n_kv_groups"], info["blocks_per_chunk"])
         if ids.shape != want:
             raise ValueError(f"block_ids must have shape {want}, got {ids.shape}")
@@ -218,16 +251,16 @@ def _batch(handle, block_ids, objects):
 
 
 def hkv_store_chunks(handle: int, pool_ptr: int, block_ids, objects, workspace_ptr: int,
-                     ws_bytes: int, stream: int = 0) -> None:
-    b, keep = _batch(handle, block_ids, objects)
+                     ws_bytes: int, stream: int = 0, info: dict | None = None) -> None:
+    b, keep = _batch(handle, block_ids, objects, info)
     _check(lib.hkv_store_chunks(handle, pool_ptr, ctypes.byref(b), workspace_ptr, ws_bytes,
                                 stream), "hkv_store_chunks")
     del keep
 
 
 def hkv_retrieve_chunks(handle: int, pool_ptr: int, block_ids, objects, workspace_ptr: int,
-                        ws_bytes: int, stream: int = 0) -> None:
-    b, keep = _batch(handle, block_ids, objects)
+                        ws_bytes: int, stream: int = 0, info: dict | None = None) -> None:
+    b, keep = _batch(handle, block_ids, objects, info)
     _check(lib.hkv_retrieve_chunks(handle, pool_ptr, ctypes.byref(b), workspace_ptr, ws_bytes,
                                    stream), "hkv_retrieve_chunks")
     del keep
@@ -273,8 +306,17 @@ class Layout:
     def workspace_size(self, max_chunks: int) -> int:
         return hkv_workspace_size(self.handle, max_chunks)
 
+    def fingerprint(self) -> int:
+        return hkv_layout_fingerprint(self.handle)
+
+    def chunk_keys(self, tokens, hash_block_tokens=0, root=0, rank_tag=0):
+        return hkv_chunk_keys(self.handle, tokens, hash_block_tokens, root, rank_tag,
+                              info=self.info)
+
     def store(self, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream=0):
-        hkv_store_chunks(self.handle, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream)
+        hkv_store_chunks(self.handle, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream,
+                         info=self.info)
 
     def retrieve(self, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream=0):
-        hkv_retrieve_chunks(self.handle, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream)
+        hkv_retrieve_chunks(self.handle, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream,
+                            info=self.info)

@@ -7,7 +7,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhkv.so")
 
-SOURCES = ["hkv_plan.cpp", "hkv_api.cpp", "hkv_copy.hip"]
+SOURCES = ["hkv_plan.cpp", "hkv_keys.cpp", "hkv_api.cpp", "hkv_copy.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]

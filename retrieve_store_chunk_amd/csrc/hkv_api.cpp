@@ -319,6 +319,24 @@ hkv_status hkv_retrieve_chunks(const hkv_layout* layout, void* pool,
   return run_copy(false, layout, pool, batch, workspace, ws_bytes, stream);
 }
 
+hkv_status hkv_layout_fingerprint(const hkv_layout* layout, uint64_t* out) {
+  if (!layout || !out) return set_error(HKV_E_ARG, "layout and out must not be NULL");
+  *out = hkv::object_fingerprint(layout->plan);
+  return HKV_OK;
+}
+
+hkv_status hkv_chunk_keys(const hkv_layout* layout, const int32_t* tokens, int64_t n_tokens,
+                          int32_t hash_block_tokens, uint64_t root, uint64_t rank_tag,
+                          uint64_t* prefix_hashes_out, uint64_t* keys_out, int32_t max_chunks,
+                          int64_t* n_chunks_out) {
+  if (!layout) return set_error(HKV_E_ARG, "layout must not be NULL");
+  std::string err;
+  hkv_status st = hkv::chunk_keys(layout->plan, tokens, n_tokens, hash_block_tokens, root,
+                                  rank_tag, prefix_hashes_out, keys_out, max_chunks,
+                                  n_chunks_out, &err);
+  return st == HKV_OK ? st : set_error(st, err);
+}
+
 const char* hkv_last_error(void) { return t_last_error.c_str(); }
 
 }  // extern "C"

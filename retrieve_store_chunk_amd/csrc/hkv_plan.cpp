@@ -139,6 +139,9 @@ hkv_status make_plan(const hkv_layout_desc& d, Plan* p, std::string* err) {
 
   p->block_size = n;
   p->blocks_per_chunk = (int32_t)k;
+  const int64_t shapes[8] = {m.kda_heads, m.kda_head_dim, m.kda_state_bytes, m.conv_dim,
+                             m.conv_kernel, m.conv_bytes, m.mla_width, m.mla_bytes};
+  std::copy(shapes, shapes + 8, p->shapes);
   p->chunk_tokens = k * n;
   p->path = d.path;
 

@@ -38,6 +38,9 @@ struct Plan {
   uint64_t pool_used = 0;
   uint64_t obj_bytes[2] = {0, 0};
   std::vector<LayerPlacement> layers;
+  // Per-rank model shapes: kda_heads, kda_head_dim, kda_state_bytes,
+  // conv_dim, conv_kernel, conv_bytes, mla_width, mla_bytes.
+  int64_t shapes[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 
   // Copy decomposition: every (layer, block j, tile s) of one chunk is one
   // work item; the same list repeats for every chunk of a call.
@@ -52,5 +55,12 @@ hkv_status unified_block_size(const hkv_model& m, int64_t* n_out, std::string* e
 
 // Full plan.  On error returns the status and sets *err.
 hkv_status make_plan(const hkv_layout_desc& d, Plan* out, std::string* err);
+
+// Object-format fingerprint and chained prefix hashes / object keys
+// (definitions in include/hkv.h).  hkv_keys.cpp.
+uint64_t object_fingerprint(const Plan& p);
+hkv_status chunk_keys(const Plan& p, const int32_t* tokens, int64_t n_tokens, int32_t hash_block,
+                      uint64_t root, uint64_t rank_tag, uint64_t* prefix_out, uint64_t* keys_out,
+                      int32_t max_chunks, int64_t* n_chunks_out, std::string* err);
 
 }  // namespace hkv

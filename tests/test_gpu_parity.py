@@ -219,3 +219,44 @@ def test_gpu_fill_matches_host_generator():
         W.gpu_fill(t.data_ptr(), n, seed, start)
         torch.cuda.synchronize()
         assert np.array_equal(t[:n].cpu().numpy(), W.fill_bytes(seed, start, n))
+
+
+def test_objects_move_between_pool_layouts_with_equal_fingerprints():
+    """Equal fingerprints mean interchangeable objects: chunks stored from a
+    path B pool are retrieved into a path A pool of the same model, matching
+    the oracle byte for byte, and storing them again from path A gives the
+    same objects."""
+    import retrieve_store_chunk_amd as hkv
+    from workloads.driver import GpuWorkload
+    cfg_b = W.make_small_config("kl_tp1")
+    cfg_a = W.make_small_config("kl_tp1")
+    cfg_a.desc = dict(cfg_a.desc, path=0)
+    gb, ga = GpuWorkload(cfg_b), GpuWorkload(cfg_a)
+    assert gb.layout.fingerprint() == ga.layout.fingerprint()
+    ref_a = oracle.Layout(cfg_a.desc)
+    gb.init_pool()
+    gb.fill_objects(1)
+    store = gb.waves[0]
+    gb.run_wave(store)
+    gb.stream.synchronize()
+    objs_b = [[gb.host_object(rc, o) for o in range(ref_a.O)] for rc in store.chunks]
+    # retrieve B's objects into A's pool at A's fresh ids
+    ga.init_pool()
+    ga.stream.synchronize()
+    used = ref_a.summary["pool_bytes_used"]
+    pool_a = ga.host_pool().copy()
+    ids_a = W.permutation(W.derive_seed(cfg_a.seed, 4242), ref_a.summary["num_blocks"])
+    ids_a = ids_a[: len(store.chunks) * ref_a.G * ref_a.k].reshape(len(store.chunks), ref_a.G,
+                                                                  ref_a.k).copy()
+    hkv.hkv_retrieve_chunks(ga.layout.handle, ga.pool.data_ptr(), ids_a,
+                            gb.object_ptrs(store.chunks), ga.ws.data_ptr(), ga.ws_bytes,
+                            ga.stream.cuda_stream)
+    ref_a.retrieve(pool_a, ids_a, objs_b)
+    assert np.array_equal(ga.host_pool()[:used], pool_a)
+    # storing from path A reproduces the objects stored from path B
+    hkv.hkv_store_chunks(ga.layout.handle, ga.pool.data_ptr(), ids_a,
+                         ga.object_ptrs(store.chunks), ga.ws.data_ptr(), ga.ws_bytes,
+                         ga.stream.cuda_stream)
+    for n, rc in enumerate(store.chunks):
+        for o in range(ref_a.O):
+            assert np.array_equal(ga.host_object(rc, o), objs_b[n][o])

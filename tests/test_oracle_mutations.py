@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from tests import golden_io
+from tests import test_keys as keys
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "hkvref.c")
@@ -65,6 +66,24 @@ MUTANTS = {
         "for (j = 0; j < lay->k - (lay->k > 1); j++) {\n"
         "                int64_t id = block_id(lay, block_ids, c, lay->kv_group[l], j);\n"
         "                const uint8_t* src"),
+    "chain_drops_the_parent_hash": (
+        "H[i] = ref_mix64((H[i - 1] ^ content) + HKVREF_GAMMA);",
+        "H[i] = ref_mix64(content + HKVREF_GAMMA);"),
+    "chunk_hash_one_fine_block_early": (
+        "uint64_t prefix = H[(c + 1) * lay->c / h];",
+        "uint64_t prefix = H[(c + 1) * lay->c / h - 1];"),
+    "block_content_ignores_token_order": (
+        "content = ref_mix64(content ^ (t | ((uint64_t)j << 32)));",
+        "content += ref_mix64(t);"),
+    "fingerprint_without_block_size": (
+        "    words[n++] = (uint64_t)lay->n;\n",
+        ""),
+    "key_ignores_object_group": (
+        "ref_mix64(base ^ (prefix + (uint64_t)(o + 1) * HKVREF_GAMMA));",
+        "ref_mix64(base ^ (prefix + HKVREF_GAMMA));"),
+    "key_ignores_parallel_config": (
+        "base = ref_mix64(hkvref_fingerprint(lay) ^ rank_tag);",
+        "base = ref_mix64(hkvref_fingerprint(lay));"),
     "conv_state_keeps_kernel_columns": (
         "int64_t conv = (int64_t)conv_dim * (conv_kernel - 1) * conv_bytes;",
         "int64_t conv = (int64_t)conv_dim * conv_kernel * conv_bytes;"),
@@ -92,6 +111,11 @@ def pin_checks():
     for case in pins.BRUTE:
         out.append(lambda c=case: pins.test_brute_force_every_injective_assignment(c))
     out += [pins.test_id_range_and_alias_errors, pins.test_random_layouts_store_retrieve_properties]
+    out += [keys.test_fine_hash_covers_exactly_its_prefix,
+            keys.test_chunk_hash_is_its_last_fine_block_hash,
+            keys.test_chain_continues_from_a_parent, keys.test_hash_depends_on_token_order_within_a_block,
+            keys.test_shared_prefix_shares_keys, keys.test_keys_separate_groups_ranks_and_roots,
+            keys.test_fingerprint_tracks_object_format_only, keys.test_bad_arguments]
     return out
 
 
