@@ -50,6 +50,27 @@ def load_traffic(config: str, tile: int, max_wg: int):
     return t.get("store_gather_bytes_per_launch")
 
 
+def wave_bytes(layout, w) -> tuple:
+    """(data bytes, object bytes) of one call.  Data bytes are page bytes that
+    hold data: every real byte of a page, none for a null id, and for an MLA
+    page of a partial chunk the rows of its valid tokens.  Object bytes are
+    the chunks' whole objects (a store writes all of them; what has no data
+    behind it is zero-filled)."""
+    import numpy as np
+    info = layout.info
+    N, k, n = info["block_size"], info["blocks_per_chunk"], len(w.chunks)
+    data = 0
+    for L in layout.layers:
+        present = w.ids[:, L["kv_group"], :] != -1
+        if L["is_mla"] and w.chunk_tokens is not None:
+            rows = np.clip(w.chunk_tokens.astype(np.int64)[:, None] - np.arange(k) * N, 0, N)
+            per = rows * (L["page_bytes"] // N)
+        else:
+            per = np.full((n, k), L["page_bytes"], dtype=np.int64)
+        data += int((per * present).sum())
+    return data, n * info["chunk_payload_bytes"]
+
+
 def cpu_baseline(cfg, min_seconds: float = 10.0, max_seconds: float = 30.0) -> dict:
     """The oracle (plain C, one thread, one memcpy per page) on a bounded
     sample of the same workload: the same layout shapes in a smaller pool,
@@ -222,8 +243,22 @@ def main() -> int:
 
     stream = g.stream
     n_w = len(g.waves)
-    per_wave_payload = [len(w.chunks) * info["chunk_payload_bytes"] for w in g.waves]
+    on_host = objects_on == "host"
+    # payload = page bytes that hold data; HBM traffic: a store reads the data
+    # and writes whole objects, a retrieve reads and writes the data; with host
+    # objects the object side crosses the host link instead of HBM
+    per_wave_payload, per_wave_hbm, per_wave_link = [], [], []
+    for w in g.waves:
+        data, objb = wave_bytes(g.layout, w)
+        per_wave_payload.append(data)
+        if w.op == "store":
+            per_wave_hbm.append(data if on_host else data + objb)
+            per_wave_link.append(objb if on_host else 0)
+        else:
+            per_wave_hbm.append(data if on_host else 2 * data)
+            per_wave_link.append(data if on_host else 0)
     step_payload = sum(per_wave_payload)
+    step_hbm = sum(per_wave_hbm)
 
     def one_step(events=None):
         for i, w in enumerate(g.waves):
@@ -255,25 +290,22 @@ def main() -> int:
     for i, w in enumerate(g.waves):
         name = "hkv_store_gather" if w.op == "store" else "hkv_retrieve_scatter"
         ms = [evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]
-        k = kern.setdefault(name, {"launches": 0, "ms": 0.0, "payload": 0})
+        k = kern.setdefault(name, {"launches": 0, "ms": 0.0, "hbm": 0, "link": 0})
         k["launches"] += args.steps
         k["ms"] += sum(ms)
-        k["payload"] += per_wave_payload[i] * args.steps
-    # Device objects: every page byte is read from and written to HBM, so the
-    # traffic is 2 x payload against the HBM peak.  Host objects: the object
-    # side crosses the host link once per byte, so payload against the link.
-    on_host = objects_on == "host"
+        k["hbm"] += per_wave_hbm[i] * args.steps
+        k["link"] += per_wave_link[i] * args.steps
     kernels = {}
     for name, k in kern.items():
         avg_ms = k["ms"] / k["launches"]
         if on_host:
-            link = k["payload"] / k["launches"]
+            link = k["link"] / k["launches"]
             kernels[name] = {"launches_per_step": k["launches"] // args.steps,
                              "avg_ms": round(avg_ms, 4),
                              "link_bytes_per_launch": int(link),
                              "link_GBs": round(link / (avg_ms / 1e3) / 1e9, 2)}
         else:
-            hbm = 2 * k["payload"] / k["launches"]  # read + write of every page
+            hbm = k["hbm"] / k["launches"]
             kernels[name] = {"launches_per_step": k["launches"] // args.steps,
                              "avg_ms": round(avg_ms, 4),
                              "hbm_bytes_per_launch": int(hbm),
@@ -309,11 +341,13 @@ def main() -> int:
         "config": {"workload": cfg.name, "title": cfg.title,
                    "chunks_per_step": sum(len(w.chunks) for w in g.waves),
                    "payload_bytes_per_step": step_payload,
+                   "hbm_bytes_per_step": step_hbm,
                    "block_size": info["block_size"], "chunk_tokens": info["chunk_tokens"],
                    "path": "B packed" if info["path"] else "A padded-unified",
                    "tile_bytes": args.tile_bytes, "max_workgroups": args.max_workgroups},
         "objects": objects_on,
-        "pct_hbm_peak": None if on_host else round(100 * 2 * value / HBM_PEAK_GBS, 2),
+        "pct_hbm_peak": None if on_host else
+        round(100 * step_hbm / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
         "pct_host_link_peak": round(100 * value / HOST_LINK_PEAK_GBS, 2) if on_host else None,
         "chunks_per_s": round(sum(len(w.chunks) for w in g.waves) / (ms_per_step / 1e3), 1),
         "kernels": kernels,

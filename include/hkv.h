@@ -174,15 +174,34 @@ typedef struct hkv_layer_info {
 /* Copies one layer's placement.  Errors: HKV_E_ARG (bad layer index). */
 hkv_status hkv_layer_info_get(const hkv_layout* layout, int32_t layer, hkv_layer_info* out);
 
+/* A block-table entry that names no page.  With a token budget of 2N or
+ * more a scheduler step spans several blocks and only its last block gets a
+ * KDA snapshot ("Kimi-Linear" recipe, Why these settings), so a KDA group's
+ * table can have holes; an MLA block past a partial chunk's last token has
+ * no page either.  Store writes zeros in a null page's place in the object (a
+ * missing state reads as zero, as the engine zeroes the initial state of a
+ * miss: vLLM hybrid KV-cache blog, section 5.3); retrieve writes nothing for
+ * it.  Null ids may repeat within a call. */
+#define HKV_NULL_BLOCK (-1)
+
 /* One call's chunks. */
 typedef struct hkv_chunk_batch {
   int32_t n_chunks;          /* >= 0; 0 is a no-op */
   const int32_t* block_ids;  /* HOST [n_chunks][G][k]: chunk c's block ids in each KV
                                 group (one block table per group, vLLM hybrid KV-cache
-                                blog, section 2.2) */
-  void* const* objects;      /* HOST [n_chunks][O] DEVICE pointers, each to obj_bytes[o]
-                                bytes, 16-byte aligned, pairwise disjoint and disjoint
-                                from the pool */
+                                blog, section 2.2), or HKV_NULL_BLOCK */
+  void* const* objects;      /* HOST [n_chunks][O] pointers the GPU can address (device
+                                memory, or pinned host memory from hipHostMalloc), each
+                                to obj_bytes[o] bytes, 16-byte aligned, pairwise disjoint
+                                and disjoint from the pool */
+  const int32_t* chunk_tokens; /* HOST [n_chunks] valid tokens per chunk (0..C), or NULL
+                                when every chunk is whole.  A partial chunk (a tail
+                                registered at a fine boundary: vLLM hybrid KV-cache blog,
+                                section 6.3; Mooncake K3 blog, fine-grained partial hits)
+                                carries in MLA page j the token rows [j*N, min(t,
+                                (j+1)*N)) only; store zeroes the rest of that page's
+                                object bytes and retrieve writes only those rows.  KDA
+                                pages are whole or null. */
 } hkv_chunk_batch;
 
 /* Device workspace bytes needed by a call with up to max_chunks chunks.
@@ -197,9 +216,11 @@ hkv_status hkv_workspace_size(const hkv_layout* layout, int32_t max_chunks, size
  * 16-byte aligned, ws_bytes >= hkv_workspace_size(n_chunks); it is
  * overwritten and must not be used by another call until the stream passes
  * this one.  stream: a hipStream_t (NULL = the default stream).
- * Repeated source ids are allowed.
- * Errors: HKV_E_ARG, HKV_E_RANGE, HKV_E_ALIAS (objects overlap each other or
- * the pool), HKV_E_ALIGN, HKV_E_WORKSPACE, HKV_E_HIP. */
+ * Repeated source ids are allowed.  Null ids and partial chunks: see
+ * HKV_NULL_BLOCK and hkv_chunk_batch.chunk_tokens.
+ * Errors: HKV_E_ARG (also a chunk_tokens entry outside [0, C]), HKV_E_RANGE
+ * (an id neither HKV_NULL_BLOCK nor in [0, num_blocks)), HKV_E_ALIAS (objects
+ * overlap each other or the pool), HKV_E_ALIGN, HKV_E_WORKSPACE, HKV_E_HIP. */
 hkv_status hkv_store_chunks(const hkv_layout* layout, const void* pool,
                             const hkv_chunk_batch* batch, void* workspace, size_t ws_bytes,
                             void* stream);
@@ -207,8 +228,10 @@ hkv_status hkv_store_chunks(const hkv_layout* layout, const void* pool,
 /* Retrieve (scatter): the inverse copy, objects -> pages of the given,
  * newly allocated block ids.  Writes exactly the real page bytes of the
  * addressed pages and nothing else (KDA padding, group slack and every other
- * block are left as they were).  Because all groups share one block-id
- * space, every id of the call must be distinct (HKV_E_ALIAS otherwise).
+ * block are left as they were; a null id writes nothing, and a partial chunk
+ * writes only its valid MLA token rows).  Because all groups share one
+ * block-id space, every non-null id of the call must be distinct
+ * (HKV_E_ALIAS otherwise).
  * Same buffer rules as hkv_store_chunks; objects are not modified.
  * Errors: HKV_E_ARG, HKV_E_RANGE, HKV_E_ALIAS, HKV_E_ALIGN, HKV_E_WORKSPACE,
  * HKV_E_HIP. */

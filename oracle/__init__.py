@@ -26,6 +26,7 @@ DESC_KEYS = (
 )
 
 OK, E_ARG, E_COVER, E_CHUNK, E_BATCH, E_POOL, E_RANGE, E_ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+NULL_BLOCK = -1
 
 _lib = None
 
@@ -67,9 +68,9 @@ def bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.hkvref_layer.restype = ctypes.c_int
     L.hkvref_layer.argtypes = [vp, i32, ctypes.POINTER(i64)]
     L.hkvref_store_chunks.restype = ctypes.c_int
-    L.hkvref_store_chunks.argtypes = [vp, vp, i32, vp, vp]
+    L.hkvref_store_chunks.argtypes = [vp, vp, i32, vp, vp, vp]
     L.hkvref_retrieve_chunks.restype = ctypes.c_int
-    L.hkvref_retrieve_chunks.argtypes = [vp, vp, i32, vp, vp]
+    L.hkvref_retrieve_chunks.argtypes = [vp, vp, i32, vp, vp, vp]
     L.hkvref_fingerprint.restype = u64
     L.hkvref_fingerprint.argtypes = [vp]
     L.hkvref_chunk_keys.restype = ctypes.c_int
@@ -192,21 +193,33 @@ class Layout:
                 if a.nbytes < self.obj_bytes(o):
                     raise ValueError("object smaller than its object group's size")
 
-    def store(self, pool: np.ndarray, block_ids, objects) -> None:
+    def _tokens(self, chunk_tokens, n):
+        if chunk_tokens is None:
+            return None, None
+        t = np.ascontiguousarray(np.asarray(chunk_tokens, dtype=np.int32))
+        if t.shape != (n,):
+            raise ValueError(f"chunk_tokens must have shape ({n},)")
+        return t, t.ctypes.data
+
+    def store(self, pool: np.ndarray, block_ids, objects, chunk_tokens=None) -> None:
         ids = self._ids(block_ids)
         n = ids.shape[0] if ids.ndim else 0
         addrs = _ptr_array(objects, n, self.O)
         self._check_buffers(pool, objects)
-        rc = self._L.hkvref_store_chunks(self._h, pool.ctypes.data, n, ids.ctypes.data, addrs)
+        keep, tp = self._tokens(chunk_tokens, n)
+        rc = self._L.hkvref_store_chunks(self._h, pool.ctypes.data, n, ids.ctypes.data, tp,
+                                         addrs)
         if rc != OK:
             raise OracleError(rc, "store_chunks")
 
-    def retrieve(self, pool: np.ndarray, block_ids, objects) -> None:
+    def retrieve(self, pool: np.ndarray, block_ids, objects, chunk_tokens=None) -> None:
         ids = self._ids(block_ids)
         n = ids.shape[0] if ids.ndim else 0
         addrs = _ptr_array(objects, n, self.O)
         self._check_buffers(pool, objects)
-        rc = self._L.hkvref_retrieve_chunks(self._h, pool.ctypes.data, n, ids.ctypes.data, addrs)
+        keep, tp = self._tokens(chunk_tokens, n)
+        rc = self._L.hkvref_retrieve_chunks(self._h, pool.ctypes.data, n, ids.ctypes.data, tp,
+                                            addrs)
         if rc != OK:
             raise OracleError(rc, "retrieve_chunks")
 

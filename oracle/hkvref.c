@@ -423,22 +423,28 @@ static int32_t block_id(const hkvref_layout* lay, const int32_t* ids, int32_t c,
 }
 
 static int check_ids(const hkvref_layout* lay, int32_t n_chunks, const int32_t* ids,
-                     int unique)
+                     const int32_t* chunk_tokens, int unique)
 {
     int64_t total = (int64_t)n_chunks * lay->n_kv_groups * lay->k, i;
     unsigned char* seen;
     for (i = 0; i < total; i++)
-        if (ids[i] < 0 || ids[i] >= lay->num_blocks)
+        if (ids[i] != HKVREF_NULL_BLOCK && (ids[i] < 0 || ids[i] >= lay->num_blocks))
             return HKVREF_E_RANGE;
+    if (chunk_tokens != NULL)
+        for (i = 0; i < n_chunks; i++)
+            if (chunk_tokens[i] < 0 || chunk_tokens[i] > lay->c)
+                return HKVREF_E_ARG;
     if (!unique)
         return HKVREF_OK;
     /* Retrieve writes every addressed page; the id space is shared by all
      * groups (vLLM hybrid KV-cache blog, sections 3.1 and 3.2), so distinct
-     * ids are what keeps the written ranges apart. */
+     * ids are what keeps the written ranges apart.  Null ids write nothing. */
     seen = (unsigned char*)calloc((size_t)lay->num_blocks, 1);
     if (seen == NULL)
         return HKVREF_E_ARG;
     for (i = 0; i < total; i++) {
+        if (ids[i] == HKVREF_NULL_BLOCK)
+            continue;
         if (seen[ids[i]]) {
             free(seen);
             return HKVREF_E_ALIAS;
@@ -449,12 +455,33 @@ static int check_ids(const hkvref_layout* lay, int32_t n_chunks, const int32_t* 
     return HKVREF_OK;
 }
 
+/* Bytes at the start of page j of layer l that hold data when the chunk has
+ * t valid tokens.  An MLA page is N token rows of equal size (vLLM hybrid
+ * KV-cache blog, section 4.2: (num_blocks, block_size, latent) view), so
+ * block j holds rows for tokens [j*N, (j+1)*N) of the chunk.  A KDA page is a
+ * whole state snapshot: all of it (a missing snapshot is a null id). */
+static int64_t valid_bytes(const hkvref_layout* lay, int32_t l, int64_t j, int64_t t)
+{
+    int64_t rows;
+    if (!lay->is_mla[l])
+        return lay->page[l];
+    rows = t - j * lay->n;
+    if (rows < 0)
+        rows = 0;
+    if (rows > lay->n)
+        rows = lay->n;
+    return rows * (lay->page[l] / lay->n);
+}
+
 /* Store: gather each chunk's pages out of the paged pool into its objects.
  * A page is copied as opaque bytes ("Kimi-Linear" recipe: LMCache treats the
- * KDA state as an opaque page; Caveats: the pages are byte-opaque). */
+ * KDA state as an opaque page; Caveats: the pages are byte-opaque).  Object
+ * bytes with no data behind them (a null id, rows past a partial chunk's last
+ * token) are written as zeros: a missing state reads as zero, as the engine
+ * zeroes the initial state of a miss (vLLM hybrid KV-cache blog, section 5.3). */
 int hkvref_store_chunks(const hkvref_layout* lay, const uint8_t* pool,
                         int32_t n_chunks, const int32_t* block_ids,
-                        uint8_t* const* objects)
+                        const int32_t* chunk_tokens, uint8_t* const* objects)
 {
     int32_t c, l;
     int64_t j;
@@ -465,17 +492,24 @@ int hkvref_store_chunks(const hkvref_layout* lay, const uint8_t* pool,
         return HKVREF_OK;
     if (pool == NULL || block_ids == NULL || objects == NULL)
         return HKVREF_E_ARG;
-    rc = check_ids(lay, n_chunks, block_ids, 0);
+    rc = check_ids(lay, n_chunks, block_ids, chunk_tokens, 0);
     if (rc != HKVREF_OK)
         return rc;
     for (c = 0; c < n_chunks; c++) {
+        int64_t t = chunk_tokens != NULL ? chunk_tokens[c] : lay->c;
         for (l = 0; l < lay->n_layers; l++) {
             uint8_t* obj = objects[(int64_t)c * lay->n_obj_groups + lay->obj_group[l]];
             for (j = 0; j < lay->k; j++) {
                 int64_t id = block_id(lay, block_ids, c, lay->kv_group[l], j);
-                const uint8_t* src = pool + lay->pool_offset[l] + id * lay->stride[l];
                 uint8_t* dst = obj + lay->obj_offset[l] + j * lay->page[l];
-                memcpy(dst, src, (size_t)lay->page[l]);
+                int64_t v;
+                if (id == HKVREF_NULL_BLOCK) {
+                    memset(dst, 0, (size_t)lay->page[l]);
+                    continue;
+                }
+                v = valid_bytes(lay, l, j, t);
+                memcpy(dst, pool + lay->pool_offset[l] + id * lay->stride[l], (size_t)v);
+                memset(dst + v, 0, (size_t)(lay->page[l] - v));
             }
         }
     }
@@ -483,10 +517,12 @@ int hkvref_store_chunks(const hkvref_layout* lay, const uint8_t* pool,
 }
 
 /* Retrieve: scatter each chunk's objects back into the pages of the given
- * (newly allocated) block ids. */
+ * (newly allocated) block ids.  Only bytes that hold data are written: a null
+ * id writes nothing, and a partial chunk's MLA pages get only their valid
+ * token rows. */
 int hkvref_retrieve_chunks(const hkvref_layout* lay, uint8_t* pool,
                            int32_t n_chunks, const int32_t* block_ids,
-                           const uint8_t* const* objects)
+                           const int32_t* chunk_tokens, const uint8_t* const* objects)
 {
     int32_t c, l;
     int64_t j;
@@ -497,17 +533,20 @@ int hkvref_retrieve_chunks(const hkvref_layout* lay, uint8_t* pool,
         return HKVREF_OK;
     if (pool == NULL || block_ids == NULL || objects == NULL)
         return HKVREF_E_ARG;
-    rc = check_ids(lay, n_chunks, block_ids, 1);
+    rc = check_ids(lay, n_chunks, block_ids, chunk_tokens, 1);
     if (rc != HKVREF_OK)
         return rc;
     for (c = 0; c < n_chunks; c++) {
+        int64_t t = chunk_tokens != NULL ? chunk_tokens[c] : lay->c;
         for (l = 0; l < lay->n_layers; l++) {
             const uint8_t* obj = objects[(int64_t)c * lay->n_obj_groups + lay->obj_group[l]];
             for (j = 0; j < lay->k; j++) {
                 int64_t id = block_id(lay, block_ids, c, lay->kv_group[l], j);
-                uint8_t* dst = pool + lay->pool_offset[l] + id * lay->stride[l];
-                const uint8_t* src = obj + lay->obj_offset[l] + j * lay->page[l];
-                memcpy(dst, src, (size_t)lay->page[l]);
+                if (id == HKVREF_NULL_BLOCK)
+                    continue;
+                memcpy(pool + lay->pool_offset[l] + id * lay->stride[l],
+                       obj + lay->obj_offset[l] + j * lay->page[l],
+                       (size_t)valid_bytes(lay, l, j, t));
             }
         }
     }

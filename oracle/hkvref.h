@@ -82,18 +82,25 @@ int hkvref_layout_summary(const hkvref_layout* lay, int64_t out[14]);
  * [8]=offset of its block-0 page inside its object. */
 int hkvref_layer(const hkvref_layout* lay, int32_t layer, int64_t out[9]);
 
+/* A block id that names no page: a missing KDA snapshot, or an MLA block
+ * past a partial chunk's last token. */
+#define HKVREF_NULL_BLOCK (-1)
+
 /* Store: for each chunk c, copy every addressed page from `pool` into the
- * chunk's objects.  block_ids is [n_chunks][G][k]; objects is
- * [n_chunks][O] host pointers.  pool is a host buffer of at least
- * summary[13] bytes. */
+ * chunk's objects.  block_ids is [n_chunks][G][k] (ids or
+ * HKVREF_NULL_BLOCK); chunk_tokens is [n_chunks] valid tokens per chunk
+ * (0..C) or NULL for whole chunks; objects is [n_chunks][O] host pointers.
+ * pool is a host buffer of at least summary[13] bytes.  Object bytes with no
+ * data (null ids, MLA rows past the last valid token) are zeroed. */
 int hkvref_store_chunks(const hkvref_layout* lay, const uint8_t* pool,
                         int32_t n_chunks, const int32_t* block_ids,
-                        uint8_t* const* objects);
+                        const int32_t* chunk_tokens, uint8_t* const* objects);
 
-/* Retrieve: the inverse copy, objects -> pages at block_ids. */
+/* Retrieve: the inverse copy, objects -> pages at block_ids; null ids and
+ * MLA rows past the last valid token are not written. */
 int hkvref_retrieve_chunks(const hkvref_layout* lay, uint8_t* pool,
                            int32_t n_chunks, const int32_t* block_ids,
-                           const uint8_t* const* objects);
+                           const int32_t* chunk_tokens, const uint8_t* const* objects);
 
 /* Object-format fingerprint: mix64-fold (f = mix64(f ^ w), f0 = GAMMA) of
  * 1, N, k, n_layers, the eight per-rank shapes (heads, head_dim,

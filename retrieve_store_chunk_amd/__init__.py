@@ -63,9 +63,12 @@ class hkv_layer_info(ctypes.Structure):
                 ("stride", u64), ("obj_offset", u64)]
 
 
+HKV_NULL_BLOCK = -1
+
+
 class hkv_chunk_batch(ctypes.Structure):
     _fields_ = [("n_chunks", i32), ("block_ids", ctypes.POINTER(i32)),
-                ("objects", ctypes.POINTER(vp))]
+                ("objects", ctypes.POINTER(vp)), ("chunk_tokens", ctypes.POINTER(i32))]
 
 
 def one_hip_runtime() -> None:
@@ -229,13 +232,19 @@ def hkv_chunk_keys(handle: int, tokens, hash_block_tokens: int = 0, root: int = 
     return prefix[:n_fine], keys[:got.value]
 
 
-def _batch(handle, block_ids, objects, info=None):
+def _batch(handle, block_ids, objects, info=None, chunk_tokens=None):
     """block_ids: int32 array [n][G][k]; objects: flat sequence of n*O device
-    addresses (chunk-major).  Shapes are checked against the layout so the
-    library never reads past the host arrays."""
+    addresses (chunk-major); chunk_tokens: None or int32 [n].  Shapes are
+    checked against the layout so the library never reads past the host
+    arrays."""
     import numpy as np
     ids = np.ascontiguousarray(block_ids, dtype=np.int32)
     n = int(ids.shape[0]) if ids.ndim else 0
+    toks = None
+    if chunk_tokens is not None:
+        toks = np.ascontiguousarray(chunk_tokens, dtype=np.int32)
+        if toks.shape != (n,):
+            raise ValueError(f"chunk_tokens must have shape ({n},), got {toks.shape}")
     if handle:
         info = info or hkv_layout_info_get(handle)
         want = (n, info["n_kv_groups"], info["blocks_per_chunk"])
@@ -246,21 +255,24 @@ def _batch(handle, block_ids, objects, info=None):
                              f"got {len(objects)}")
     addrs = (vp * max(1, len(objects)))(*[int(a) for a in objects])
     b = hkv_chunk_batch(n, ids.ctypes.data_as(ctypes.POINTER(i32)),
-                        ctypes.cast(addrs, ctypes.POINTER(vp)))
-    return b, (ids, addrs)
+                        ctypes.cast(addrs, ctypes.POINTER(vp)),
+                        None if toks is None else toks.ctypes.data_as(ctypes.POINTER(i32)))
+    return b, (ids, addrs, toks)
 
 
 def hkv_store_chunks(handle: int, pool_ptr: int, block_ids, objects, workspace_ptr: int,
-                     ws_bytes: int, stream: int = 0, info: dict | None = None) -> None:
-    b, keep = _batch(handle, block_ids, objects, info)
+                     ws_bytes: int, stream: int = 0, info: dict | None = None,
+                     chunk_tokens=None) -> None:
+    b, keep = _batch(handle, block_ids, objects, info, chunk_tokens)
     _check(lib.hkv_store_chunks(handle, pool_ptr, ctypes.byref(b), workspace_ptr, ws_bytes,
                                 stream), "hkv_store_chunks")
     del keep
 
 
 def hkv_retrieve_chunks(handle: int, pool_ptr: int, block_ids, objects, workspace_ptr: int,
-                        ws_bytes: int, stream: int = 0, info: dict | None = None) -> None:
-    b, keep = _batch(handle, block_ids, objects, info)
+                        ws_bytes: int, stream: int = 0, info: dict | None = None,
+                        chunk_tokens=None) -> None:
+    b, keep = _batch(handle, block_ids, objects, info, chunk_tokens)
     _check(lib.hkv_retrieve_chunks(handle, pool_ptr, ctypes.byref(b), workspace_ptr, ws_bytes,
                                    stream), "hkv_retrieve_chunks")
     del keep
@@ -313,10 +325,12 @@ class Layout:
         return hkv_chunk_keys(self.handle, tokens, hash_block_tokens, root, rank_tag,
                               info=self.info)
 
-    def store(self, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream=0):
+    def store(self, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream=0,
+              chunk_tokens=None):
         hkv_store_chunks(self.handle, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream,
-                         info=self.info)
+                         info=self.info, chunk_tokens=chunk_tokens)
 
-    def retrieve(self, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream=0):
+    def retrieve(self, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream=0,
+                 chunk_tokens=None):
         hkv_retrieve_chunks(self.handle, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream,
-                            info=self.info)
+                            info=self.info, chunk_tokens=chunk_tokens)

@@ -167,13 +167,21 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   const int32_t* ids = b->block_ids;
   const uint64_t n_ids = n * G * k;
   for (uint64_t i = 0; i < n_ids; ++i)
-    if (ids[i] < 0 || ids[i] >= p.num_blocks)
+    if (ids[i] != HKV_NULL_BLOCK && (ids[i] < 0 || ids[i] >= p.num_blocks))
       return set_error(HKV_E_RANGE, "block id " + std::to_string(ids[i]) + " outside [0, " +
                                         std::to_string(p.num_blocks) + ")");
+  if (b->chunk_tokens)
+    for (uint64_t c = 0; c < n; ++c)
+      if (b->chunk_tokens[c] < 0 || b->chunk_tokens[c] > p.chunk_tokens)
+        return set_error(HKV_E_ARG, "chunk_tokens[" + std::to_string(c) + "] = " +
+                                        std::to_string(b->chunk_tokens[c]) + " outside [0, " +
+                                        std::to_string(p.chunk_tokens) + "]");
   if (!store) {
     // One block-id space for all groups: distinct ids <=> disjoint writes.
+    // Null ids write nothing.
     std::vector<uint8_t> seen((size_t)p.num_blocks, 0);
     for (uint64_t i = 0; i < n_ids; ++i) {
+      if (ids[i] == HKV_NULL_BLOCK) continue;
       if (seen[(size_t)ids[i]])
         return set_error(HKV_E_ALIAS, "retrieve target block id " + std::to_string(ids[i]) +
                                           " appears twice in one call");
@@ -202,6 +210,7 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
     std::memcpy(h + wl.ids_off, ids, n_ids * sizeof(int32_t));
     uint64_t* objs = reinterpret_cast<uint64_t*>(h + wl.objs_off);
     for (uint64_t i = 0; i < n * O; ++i) objs[i] = reinterpret_cast<uintptr_t>(b->objects[i]);
+    if (b->chunk_tokens) std::memcpy(h + wl.tokens_off, b->chunk_tokens, n * sizeof(int32_t));
   });
   if (st != HKV_OK) return st;
 
@@ -211,7 +220,10 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   a.items = reinterpret_cast<const uint64_t*>(wsb + wl.items_off);
   a.ids = reinterpret_cast<const int32_t*>(wsb + wl.ids_off);
   a.objs = reinterpret_cast<const uint64_t*>(wsb + wl.objs_off);
+  a.chunk_tokens =
+      b->chunk_tokens ? reinterpret_cast<const int32_t*>(wsb + wl.tokens_off) : nullptr;
   a.total_items = n * per_chunk;
+  a.block_tokens = (uint64_t)p.block_size;
   a.tile_bytes = p.tile_bytes;
   a.items_per_chunk = (uint32_t)per_chunk;
   a.n_kv_groups = (uint32_t)G;

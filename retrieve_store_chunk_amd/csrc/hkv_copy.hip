@@ -98,6 +98,19 @@ __device__ __forceinline__ void copy_span(uint8_t* dst, const uint8_t* src, uint
   }
 }
 
+// Writes `bytes` zero bytes at dst with all kThreads lanes of the workgroup.
+__device__ __forceinline__ void zero_span(uint8_t* dst, uint32_t bytes) {
+  const uint32_t t = threadIdx.x;
+  if (((reinterpret_cast<uintptr_t>(dst) | bytes) & 15u) == 0) {
+    HKV_GLOBAL v4u* d = (HKV_GLOBAL v4u*)dst;
+    const v4u z = {0u, 0u, 0u, 0u};
+    for (uint32_t i = t; i < (bytes >> 4); i += kThreads) store16(d + i, z);
+  } else {
+    HKV_GLOBAL uint8_t* d = (HKV_GLOBAL uint8_t*)dst;
+    for (uint32_t i = t; i < bytes; i += kThreads) d[i] = 0;
+  }
+}
+
 template <bool kStore>
 __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a) {
   const HKV_CONST hkv::DevLayer* layers = (const HKV_CONST hkv::DevLayer*)a.layers;
@@ -123,17 +136,30 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a) {
     const uint32_t s = (uint32_t)(w >> 32);
     const HKV_CONST hkv::DevLayer* L = layers + l;
     const uint64_t page_bytes = L->page;
-    const int64_t id = ids[((uint64_t)c * a.n_kv_groups + L->kv_group) * a.blocks_per_chunk + j];
+    const int32_t id = ids[((uint64_t)c * a.n_kv_groups + L->kv_group) * a.blocks_per_chunk + j];
     uint8_t* obj = reinterpret_cast<uint8_t*>(objs[(uint64_t)c * a.n_obj_groups + L->obj_group]);
     const uint64_t off = (uint64_t)s * a.tile_bytes;
     const uint64_t rest = page_bytes - off;
     const uint32_t bytes = (uint32_t)(rest < a.tile_bytes ? rest : a.tile_bytes);
-    uint8_t* page = a.pool + L->pool_offset + (uint64_t)id * L->stride + off;
-    uint8_t* dst_obj = obj + L->obj_offset + (uint64_t)j * page_bytes + off;
-    if (kStore)
-      copy_span(dst_obj, page, bytes);
-    else
-      copy_span(page, dst_obj, bytes);
+    uint8_t* obj_tile = obj + L->obj_offset + (uint64_t)j * page_bytes + off;
+    // Bytes of this page that hold data: all of it, none for a null id, and
+    // for an MLA page of a partial chunk the rows of its valid tokens.
+    uint64_t valid = id < 0 ? 0 : page_bytes;
+    if (a.chunk_tokens && L->row_bytes && id >= 0) {
+      int64_t rows = (int64_t)a.chunk_tokens[c] - (int64_t)j * (int64_t)a.block_tokens;
+      rows = rows < 0 ? 0 : (rows > (int64_t)a.block_tokens ? (int64_t)a.block_tokens : rows);
+      valid = (uint64_t)rows * L->row_bytes;
+    }
+    const uint32_t live =
+        valid > off ? (uint32_t)(valid - off < bytes ? valid - off : bytes) : 0u;
+    if (live) {
+      uint8_t* page = a.pool + L->pool_offset + (uint64_t)id * L->stride + off;
+      if (kStore)
+        copy_span(obj_tile, page, live);
+      else
+        copy_span(page, obj_tile, live);
+    }
+    if (kStore && live < bytes) zero_span(obj_tile + live, bytes - live);
   }
 }
 

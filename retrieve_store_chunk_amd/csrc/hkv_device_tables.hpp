@@ -15,7 +15,9 @@ struct DevLayer {
   uint64_t page;         // real bytes of one page
   uint32_t kv_group;
   uint32_t obj_group;
-  uint64_t reserved_;    // keeps the struct 16-byte sized for the uploads
+  uint32_t row_bytes;    // MLA: bytes per token row (a partial chunk keeps whole rows);
+                         // KDA: 0 (a state page is whole or null)
+  uint32_t pad_;
 };
 static_assert(sizeof(DevLayer) == 48, "DevLayer layout");
 
@@ -32,7 +34,9 @@ struct CopyArgs {
   const uint64_t* items;   // [items_per_chunk]
   const int32_t* ids;      // [n_chunks][G][k]
   const uint64_t* objs;    // [n_chunks][O] device addresses
+  const int32_t* chunk_tokens;  // [n_chunks] valid tokens, or nullptr: all chunks whole
   uint64_t total_items;    // n_chunks * items_per_chunk
+  uint64_t block_tokens;   // N
   uint64_t tile_bytes;
   uint32_t items_per_chunk;
   uint32_t n_kv_groups;
@@ -42,7 +46,7 @@ struct CopyArgs {
 
 // Workspace sections, each starting on a 256-byte boundary.
 struct WorkspaceLayout {
-  uint64_t layers_off, items_off, ids_off, objs_off, total;
+  uint64_t layers_off, items_off, ids_off, objs_off, tokens_off, total;
 };
 
 inline constexpr uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -54,7 +58,8 @@ inline WorkspaceLayout workspace_layout(uint64_t n_layers, uint64_t n_items, uin
   w.items_off = w.layers_off + align256(n_layers * sizeof(DevLayer));
   w.ids_off = w.items_off + align256(n_items * sizeof(uint64_t));
   w.objs_off = w.ids_off + align256(n_chunks * G * k * sizeof(int32_t));
-  w.total = w.objs_off + align256(n_chunks * O * sizeof(uint64_t));
+  w.tokens_off = w.objs_off + align256(n_chunks * O * sizeof(uint64_t));
+  w.total = w.tokens_off + align256(n_chunks * sizeof(int32_t));
   return w;
 }
 

@@ -243,6 +243,7 @@ hkv_status make_plan(const hkv_layout_desc& d, Plan* p, std::string* err) {
     dl.page = x.page;
     dl.kv_group = (uint32_t)x.kv_group;
     dl.obj_group = (uint32_t)x.obj_group;
+    dl.row_bytes = x.is_mla ? (uint32_t)s.tok_bytes : 0;
     p->dev_layers.push_back(dl);
     const uint64_t tiles = x.page ? (x.page + tile - 1) / tile : 0;
     for (int64_t j = 0; j < k; ++j)

@@ -159,8 +159,10 @@ def test_call_validation_on_host():
         bad = ids.copy()
         bad[1, 0, 0] = nb
         assert st(fn, ids=bad) == hkv.HKV_E_RANGE
-        bad[1, 0, 0] = -1
+        bad[1, 0, 0] = -2  # -1 is HKV_NULL_BLOCK
         assert st(fn, ids=bad) == hkv.HKV_E_RANGE
+        assert hkv.status_of(fn, lay.handle, pool, ids, objs, ws, ws_bytes, 0, None,
+                             [1, lay.info["chunk_tokens"] + 1]) == hkv.HKV_E_ARG
         # overlapping objects / object inside the pool / workspace in the pool
         assert st(fn, objs=[objs[0]] * len(objs)) == hkv.HKV_E_ALIAS
         assert st(fn, objs=[pool + used - 256] + objs[1:]) == hkv.HKV_E_ALIAS

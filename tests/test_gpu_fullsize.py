@@ -65,6 +65,16 @@ def test_full_size_sampled(name):
         L = Ls[l]
         return L["pool_offset"] + int(block) * L["stride"], L["page_bytes"]
 
+    N = ref.summary["block_size"]
+
+    def valid(l, j, w, ci):
+        """Bytes of page j of layer l that hold data for chunk ci of wave w."""
+        L = Ls[l]
+        if not L["is_mla"] or w.chunk_tokens is None:
+            return L["page_bytes"]
+        rows = min(N, max(0, int(w.chunk_tokens[ci]) - j * N))
+        return rows * (L["page_bytes"] // N)
+
     def on_wave(i, w):
         nonlocal retrieved_since_fill
         if w.op == "store" and w.pool_seed is not None:
@@ -79,23 +89,37 @@ def test_full_size_sampled(name):
             L = Ls[l]
             o, grp = L["obj_group"], L["kv_group"]
             obj_lo = L["obj_offset"] + j * L["page_bytes"]
+            bid = int(w.ids[ci, grp, j])
             if w.op == "store":
-                off, nbytes = page_at(l, w.ids[ci, grp, j])
+                if bid == W.NULL_BLOCK:   # a null page is zeros in the object
+                    got = _d2h(g.object_view(rc, o), obj_lo, L["page_bytes"])
+                    assert not got.any(), f"store wave {i} chunk {rc} layer {l} j {j}: null"
+                    continue
+                off, nbytes = page_at(l, bid)
+                v = valid(l, j, w, ci)
                 want = W.fill_bytes(g.pool_seed_of[rc], off, nbytes)
                 got = _d2h(g.object_view(rc, o), obj_lo, nbytes)
-                assert np.array_equal(got, want), f"store wave {i} chunk {rc} layer {l} j {j}"
+                assert np.array_equal(got[:v], want[:v]), \
+                    f"store wave {i} chunk {rc} layer {l} j {j}"
+                assert not got[v:].any()
                 # the source page is unchanged
                 assert np.array_equal(_d2h(g.pool, off, nbytes), want)
             else:
+                if bid == W.NULL_BLOCK:
+                    continue
+                v = valid(l, j, w, ci)
                 if w.prefilled_objects:
-                    want = W.fill_bytes(W.derive_seed(W.object_seed(cfg, *rc), o), obj_lo,
-                                        L["page_bytes"])
+                    want = W.fill_bytes(W.derive_seed(W.object_seed(cfg, *rc), o), obj_lo, v)
                 else:
-                    soff, nbytes = page_at(l, g.store_ids[rc][grp, j])
-                    want = W.fill_bytes(g.pool_seed_of[rc], soff, nbytes)
-                off, nbytes = page_at(l, w.ids[ci, grp, j])
-                got = _d2h(g.pool, off, nbytes)
+                    soff, _ = page_at(l, g.store_ids[rc][grp, j])
+                    want = W.fill_bytes(g.pool_seed_of[rc], soff, v)
+                off, nbytes = page_at(l, bid)
+                got = _d2h(g.pool, off, v)
                 assert np.array_equal(got, want), f"retrieve wave {i} chunk {rc} layer {l} j {j}"
+                # rows past a partial chunk's last token are not written
+                if v < nbytes and bid in fresh:
+                    assert np.array_equal(_d2h(g.pool, off + v, nbytes - v),
+                                          W.fill_bytes(fill_seed, off + v, nbytes - v))
                 # padding (path A) / slack (path B) after the page is untouched
                 if path == 0 and L["reserved_bytes"] > nbytes and \
                         int(w.ids[ci, grp, j]) in fresh:
@@ -113,12 +137,12 @@ def test_full_size_sampled(name):
             for ci in {0, len(w.chunks) - 1}:
                 for grp, tot in totals.items():
                     b = int(w.ids[ci, grp, 0])
-                    if tot < stride and b in fresh:
+                    if tot < stride and b in fresh and b != W.NULL_BLOCK:
                         lo = b * stride + tot
                         assert np.array_equal(_d2h(g.pool, lo, stride - tot),
                                               W.fill_bytes(fill_seed, lo, stride - tot))
         if w.op == "retrieve":
-            retrieved_since_fill |= set(w.ids.reshape(-1).tolist())
+            retrieved_since_fill |= set(w.ids.reshape(-1).tolist()) - {W.NULL_BLOCK}
         # blocks no retrieve has written since the last fill still hold the fill
         free = [b for b in range(g.info["num_blocks"]) if b not in retrieved_since_fill]
         for b in rng.choice(free, size=min(4, len(free)), replace=False):

@@ -61,7 +61,8 @@ def run_parity(cfg, tile_bytes=0, max_workgroups=0, pool_fill=None, objects="dev
         g.run_wave(w)
         g.stream.synchronize()
         objs = [objs_ref[rc] for rc in w.chunks]
-        (ref.store if w.op == "store" else ref.retrieve)(pool_ref, w.ids, objs)
+        (ref.store if w.op == "store" else ref.retrieve)(pool_ref, w.ids, objs,
+                                                         chunk_tokens=w.chunk_tokens)
         got = g.host_pool()
         assert np.array_equal(got, pool_ref), f"pool differs after wave {i} ({w.op})"
     for rc in g.slot_of:
@@ -74,7 +75,7 @@ def run_parity(cfg, tile_bytes=0, max_workgroups=0, pool_fill=None, objects="dev
     return n_waves
 
 
-@pytest.mark.parametrize("name", W.CONFIG_NAMES)
+@pytest.mark.parametrize("name", W.CONFIG_NAMES + ("k3_tp8_holes", "kl_tp1_tails"))
 def test_workload_parity_small(name):
     """The five workloads with their real page shapes, smaller pools and
     fewer requests: several waves, several tiles per page, ragged last tiles."""
@@ -151,6 +152,29 @@ EDGE = [
 def test_edge_layouts(cfg):
     run_parity(cfg)
     run_parity(cfg, tile_bytes=4096, max_workgroups=3)
+
+
+def holes_and_tails(cfg, every, tail):
+    """The same layout with KDA snapshots every `every` blocks and a partial
+    last chunk of `tail` tokens in every request."""
+    import copy
+    cfg = copy.deepcopy(cfg)
+    tails = {(r, n - 1): tail for r, n in enumerate(cfg.requests)}
+    cfg.phases = [W.Phase(ph.op, ph.chunks, ph.prefilled_objects, every, tails)
+                  for ph in cfg.phases]
+    cfg.name += f"_every{every}_tail{tail}"
+    return cfg
+
+
+@pytest.mark.parametrize("cfg", [holes_and_tails(EDGE[0], 2, 5), holes_and_tails(EDGE[1], 1, 1),
+                                 holes_and_tails(EDGE[2], 3, 33),
+                                 holes_and_tails(EDGE[9], 2, 17)],
+                         ids=lambda c: c.name)
+def test_edge_layouts_with_holes_and_tails(cfg):
+    """Null ids and partial chunks on odd page sizes (byte path), several
+    blocks per chunk and multi-tile pages (4 KiB tiles)."""
+    run_parity(cfg)
+    run_parity(cfg, tile_bytes=4096, max_workgroups=5)
 
 
 @pytest.mark.parametrize("name", ["tiny", "kl_tp1_host", "k3_tp8", "long_ctx"])

@@ -42,11 +42,19 @@ MUTANTS = {
         "while (n * tok_bytes < kda_page)",
         "while (n * tok_bytes <= kda_page)"),
     "retrieve_writes_padding": (
-        "const uint8_t* src = obj + lay->obj_offset[l] + j * lay->page[l];\n"
-        "                memcpy(dst, src, (size_t)lay->page[l]);",
-        "const uint8_t* src = obj + lay->obj_offset[l] + j * lay->page[l];\n"
-        "                memcpy(dst, src, (size_t)(lay->reserved[l] < lay->obj_bytes[lay->obj_group[l]]"
-        " - lay->obj_offset[l] - j * lay->page[l] ? lay->reserved[l] : lay->page[l]));"),
+        "                       (size_t)valid_bytes(lay, l, j, t));",
+        "                       (size_t)valid_bytes(lay, l, j, t));\n"
+        "                memset(pool + lay->pool_offset[l] + id * lay->stride[l] + lay->page[l], 0,"
+        " (size_t)(lay->reserved[l] - lay->page[l]));"),
+    "retrieve_ignores_partial_rows": (
+        "                       (size_t)valid_bytes(lay, l, j, t));",
+        "                       (size_t)lay->page[l]);"),
+    "null_page_not_zeroed_on_store": (
+        "                    memset(dst, 0, (size_t)lay->page[l]);\n                    continue;",
+        "                    continue;"),
+    "partial_rows_counted_from_block_start": (
+        "    rows = t - j * lay->n;",
+        "    rows = t;"),
     "object_groups_swapped": (
         "lay->obj_group[l] = lay->is_mla[l] ? 1 : 0;",
         "lay->obj_group[l] = lay->is_mla[l] ? 0 : 1;"),
@@ -60,12 +68,12 @@ MUTANTS = {
         "if (lay->index_in_group[l] + 1 > slabs)",
         "if (lay->index_in_group[l] > slabs)"),
     "last_block_of_chunk_skipped": (
-        "for (j = 0; j < lay->k; j++) {\n"
+        "            for (j = 0; j < lay->k; j++) {\n"
         "                int64_t id = block_id(lay, block_ids, c, lay->kv_group[l], j);\n"
-        "                const uint8_t* src",
-        "for (j = 0; j < lay->k - (lay->k > 1); j++) {\n"
+        "                uint8_t* dst",
+        "            for (j = 0; j < lay->k - (lay->k > 1); j++) {\n"
         "                int64_t id = block_id(lay, block_ids, c, lay->kv_group[l], j);\n"
-        "                const uint8_t* src"),
+        "                uint8_t* dst"),
     "chain_drops_the_parent_hash": (
         "H[i] = ref_mix64((H[i - 1] ^ content) + HKVREF_GAMMA);",
         "H[i] = ref_mix64(content + HKVREF_GAMMA);"),
@@ -110,7 +118,8 @@ def pin_checks():
     out.append(pins.test_mla_object_is_chunk_tokens_by_latent_array)
     for case in pins.BRUTE:
         out.append(lambda c=case: pins.test_brute_force_every_injective_assignment(c))
-    out += [pins.test_id_range_and_alias_errors, pins.test_random_layouts_store_retrieve_properties]
+    out += [pins.test_id_range_and_alias_errors, pins.test_whole_chunks_and_no_nulls_reduce_to_plain_copies,
+            pins.test_random_layouts_store_retrieve_properties, pins.test_null_ids_and_partial_chunks]
     out += [keys.test_fine_hash_covers_exactly_its_prefix,
             keys.test_chunk_hash_is_its_last_fine_block_hash,
             keys.test_chain_continues_from_a_parent, keys.test_hash_depends_on_token_order_within_a_block,

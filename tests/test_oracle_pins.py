@@ -17,7 +17,7 @@ import oracle
 import workloads
 from tests import golden_io
 from tests.invariants import (check_live_pages_disjoint, check_objects, check_path_a,
-                              check_path_b, objects_by_views, payload_bytes)
+                              check_path_b, layer_views, objects_by_views, payload_bytes)
 
 E = {"E_CHUNK": oracle.E_CHUNK, "E_BATCH": oracle.E_BATCH, "E_COVER": oracle.E_COVER}
 
@@ -404,11 +404,20 @@ def test_id_range_and_alias_errors():
         with pytest.raises(oracle.OracleError) as e:
             fn(pool, bad, objs)
         assert e.value.status == oracle.E_RANGE
-        bad[1, 0, 0] = -1
+        bad[1, 0, 0] = -2          # -1 is the null id; other negatives are out of range
         with pytest.raises(oracle.OracleError) as e:
             fn(pool, bad, objs)
         assert e.value.status == oracle.E_RANGE
         bad[1, 0, 0] = nb
+        with pytest.raises(oracle.OracleError) as e:
+            fn(pool, ids, objs, chunk_tokens=[1, lay.summary["chunk_tokens"] + 1])
+        assert e.value.status == oracle.E_ARG
+        with pytest.raises(oracle.OracleError) as e:
+            fn(pool, ids, objs, chunk_tokens=[-1, 1])
+        assert e.value.status == oracle.E_ARG
+    nulls = ids.copy()
+    nulls[0, 0, 0] = nulls[1, 0, 0] = oracle.NULL_BLOCK
+    lay.retrieve(pool, nulls, objs)  # null ids may repeat: they write nothing
     dup = ids.copy()
     dup[1, 0, 0] = dup[0, 0, 0]
     lay.store(pool, dup, objs)  # repeated sources are fine
@@ -426,3 +435,94 @@ def test_pool_too_small():
     with pytest.raises(oracle.OracleError) as e:
         oracle.Layout(d)
     assert e.value.status == oracle.E_POOL
+
+
+# ---------------------------------------------------------------- holes and tails
+def _rows(L, summary):
+    """(rows per page, bytes per row) of an MLA layer."""
+    N = summary["block_size"]
+    return N, L["page_bytes"] // N
+
+
+@settings(max_examples=120, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(layout_params, st.integers(0, 2**31 - 1), st.floats(0, 0.6))
+def test_null_ids_and_partial_chunks(params, seed, null_frac):
+    """A null id names no page: store writes zeros in its place, retrieve
+    writes nothing.  A chunk with t valid tokens carries, in MLA page j, the
+    rows of tokens [j*N, min(t, (j+1)*N)) (the (num_blocks, N, latent) view of
+    vLLM hybrid KV-cache blog, section 4.2); store zeroes the rest of the
+    page's object bytes, retrieve writes only those rows.  KDA pages are whole
+    or null."""
+    is_mla, path, sep, grouping, cmin, pf, conv = params
+    d = small_desc(is_mla, path, sep, grouping, cmin, pf, conv_dim=conv)
+    lay = oracle.Layout(d)
+    s = lay.summary
+    per_chunk = lay.G * lay.k
+    max_chunks = s["num_blocks"] // per_chunk
+    if max_chunks == 0:
+        return
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, max_chunks + 1))
+    C, N = s["chunk_tokens"], s["block_size"]
+    used = s["pool_bytes_used"]
+    pool = rng.integers(0, 256, used, dtype=np.uint8)
+    ids = rng.permutation(s["num_blocks"])[:n * per_chunk].astype(np.int32)
+    ids = ids.reshape(n, lay.G, lay.k)
+    ids[rng.random(ids.shape) < null_frac] = oracle.NULL_BLOCK
+    toks = rng.integers(0, C + 1, n).astype(np.int32)
+    toks[rng.random(n) < 0.3] = C
+    objs = [[rng.integers(0, 256, lay.obj_bytes(o), dtype=np.uint8) for o in range(lay.O)]
+            for _ in range(n)]
+    lay.store(pool, ids, objs, chunk_tokens=toks)
+    views = layer_views(lay.layers, s["num_blocks"], pool)
+    expect_written = 0
+    for c in range(n):
+        for l, L in enumerate(lay.layers):
+            for j in range(lay.k):
+                page = objs[c][L["obj_group"]][L["obj_offset"] + j * L["page_bytes"]:
+                                               L["obj_offset"] + (j + 1) * L["page_bytes"]]
+                b = ids[c, L["kv_group"], j]
+                if b == oracle.NULL_BLOCK:
+                    assert not page.any()
+                    continue
+                if L["is_mla"]:
+                    rows, rb = _rows(L, s)
+                    v = max(0, min(N, int(toks[c]) - j * N)) * rb
+                else:
+                    v = L["page_bytes"]
+                assert np.array_equal(page[:v], views[l][b][:v])
+                assert not page[v:].any()
+                expect_written += v
+    # retrieve into fresh ids on two backgrounds: exactly the valid bytes land
+    fresh = rng.permutation(s["num_blocks"])[:n * per_chunk].astype(np.int32)
+    fresh = fresh.reshape(n, lay.G, lay.k)
+    fresh[ids == oracle.NULL_BLOCK] = oracle.NULL_BLOCK
+    lo = np.zeros(used, np.uint8)
+    hi = np.full(used, 0xFF, np.uint8)
+    lay.retrieve(lo, fresh, objs, chunk_tokens=toks)
+    lay.retrieve(hi, fresh, objs, chunk_tokens=toks)
+    written = (lo != 0) | (hi != 0xFF)
+    assert int(written.sum()) == expect_written
+    # ... and storing them again reproduces the objects
+    again = [[np.full(lay.obj_bytes(o), 7, np.uint8) for o in range(lay.O)] for _ in range(n)]
+    lay.store(lo, fresh, again, chunk_tokens=toks)
+    for c in range(n):
+        for o in range(lay.O):
+            assert np.array_equal(again[c][o], objs[c][o])
+
+
+def test_whole_chunks_and_no_nulls_reduce_to_plain_copies():
+    d = small_desc([0, 1, 0, 1], 1, 1, "default", 20, 5)
+    lay = oracle.Layout(d)
+    s = lay.summary
+    rng = np.random.default_rng(5)
+    pool = rng.integers(0, 256, s["pool_bytes_used"], dtype=np.uint8)
+    ids = rng.permutation(s["num_blocks"])[:2 * lay.G * lay.k].astype(np.int32)
+    ids = ids.reshape(2, lay.G, lay.k)
+    a = [[np.zeros(lay.obj_bytes(o), np.uint8) for o in range(lay.O)] for _ in range(2)]
+    b = [[np.ones(lay.obj_bytes(o), np.uint8) for o in range(lay.O)] for _ in range(2)]
+    lay.store(pool, ids, a)
+    lay.store(pool, ids, b, chunk_tokens=[s["chunk_tokens"]] * 2)
+    for c in range(2):
+        for o in range(lay.O):
+            assert np.array_equal(a[c][o], b[c][o])

@@ -176,6 +176,13 @@ class Phase:
     op: str                       # "store" or "retrieve"
     chunks: list                  # [(request, chunk_index)] in request then chunk order
     prefilled_objects: bool = False  # retrieve of objects that no store in this run made
+    # KDA snapshots exist only at every snapshot_every-th block boundary of a
+    # request (a scheduler step spanning several blocks snapshots only its
+    # last one); other KDA block-table entries are null.
+    snapshot_every: int = 1
+    # (request, chunk) -> valid tokens of a partial chunk (a tail); KDA blocks
+    # not completed inside it and MLA blocks past its last token are null.
+    tail_tokens: dict = field(default_factory=dict)
 
 
 @dataclass
@@ -261,12 +268,36 @@ def make_config(name: str) -> Config:
                       notes="16 requests x 8 chunks stored to host objects (7.5 GB pinned), "
                             "the first 4 chunks of each retrieved from them",
                       extra={"objects": "host"})
+    if name == "k3_tp8_holes":
+        seed = 0x48B0007
+        req = [4] * 256
+        desc = _desc(K3_93, 6, 128, 2304, 1, 0, 24 * GIB, block_size=768, chunk_min=1500,
+                     max_batched=4 * 768)
+        every = 4  # a 4N token budget: each step advances 4 blocks, snapshots its last
+        return Config(name, "K3-shaped TP=8 rank, token budget 4N: KDA snapshots at every "
+                      "4th block only", desc, req,
+                      [Phase("store", _all_chunks(req), snapshot_every=every),
+                       Phase("retrieve", _all_chunks(req), snapshot_every=every)], seed,
+                      notes="the K3 workload with a scheduler budget of 4N (allowed with "
+                            "separate object groups): 3 of every 4 KDA block-table entries "
+                            "are null")
+    if name == "kl_tp1_tails":
+        seed = 0x48B0008
+        req = [2] * 256
+        desc = _desc(KIMI_LINEAR_27, 32, 128, 12288, 2, 1, 64 * GIB)
+        tails = {(r, 1): 2048 - 1888 for r in range(256)}
+        return Config(name, "Kimi-Linear TP=1, path B: 256 requests of 2048 tokens = one "
+                      "whole chunk + a 160-token partial tail", desc, req,
+                      [Phase("store", _all_chunks(req), tail_tokens=tails),
+                       Phase("retrieve", _all_chunks(req), tail_tokens=tails)], seed,
+                      notes="each request stores its whole first chunk and a partial second "
+                            "chunk (160 MLA rows, no KDA snapshot: its block is not complete)")
     raise KeyError(name)
 
 
 CONFIG_NAMES = ("tiny", "kl_tp2", "kl_tp1", "k3_tp8", "long_ctx")
 # Further workloads beyond the five above.
-EXTRA_CONFIG_NAMES = ("kl_tp1_host",)
+EXTRA_CONFIG_NAMES = ("kl_tp1_host", "k3_tp8_holes", "kl_tp1_tails")
 
 
 def make_small_config(name: str) -> Config:
@@ -296,6 +327,17 @@ def make_small_config(name: str) -> Config:
         cfg.requests = [4] * 3
         cfg.phases = [Phase("store", _all_chunks(cfg.requests)),
                       Phase("retrieve", _all_chunks(cfg.requests, first=2))]
+    elif name == "k3_tp8_holes":
+        cfg.desc["pool_bytes"] = 512 * MIB
+        cfg.requests = [4] * 3
+        cfg.phases = [Phase("store", _all_chunks(cfg.requests), snapshot_every=4),
+                      Phase("retrieve", _all_chunks(cfg.requests), snapshot_every=4)]
+    elif name == "kl_tp1_tails":
+        cfg.desc["pool_bytes"] = 1 * GIB
+        cfg.requests = [2] * 8
+        tails = {(r, 1): 160 for r in range(8)}
+        cfg.phases = [Phase("store", _all_chunks(cfg.requests), tail_tokens=tails),
+                      Phase("retrieve", _all_chunks(cfg.requests), tail_tokens=tails)]
     elif name == "long_ctx":
         cfg.desc["pool_bytes"] = 1 * GIB
         cfg.requests = [8] + [1] * 8
@@ -308,13 +350,17 @@ def make_small_config(name: str) -> Config:
 # --------------------------------------------------------------------------
 # Waves and block tables
 # --------------------------------------------------------------------------
+NULL_BLOCK = -1
+
+
 @dataclass
 class Wave:
     op: str
     chunks: list          # [(request, chunk_index)]
-    ids: np.ndarray       # int32 [n_chunks][G][k]
+    ids: np.ndarray       # int32 [n_chunks][G][k] (NULL_BLOCK for a missing page)
     pool_seed: int | None  # store waves: the pool is (re)filled with this seed first
     prefilled_objects: bool = False
+    chunk_tokens: np.ndarray | None = None  # int32 [n_chunks] valid tokens; None: all whole
 
 
 def object_seed(cfg: Config, request: int, chunk: int) -> int:
@@ -344,12 +390,15 @@ def _split_waves(chunks, max_chunks: int):
     return waves
 
 
-def plan_waves(cfg: Config, num_blocks: int, n_kv_groups: int, blocks_per_chunk: int) -> list:
+def plan_waves(cfg: Config, num_blocks: int, n_kv_groups: int, blocks_per_chunk: int,
+               kda_groups=(), block_tokens: int = 0, chunk_tokens: int = 0) -> list:
     """Block tables for every wave.  Ids are assigned from a Fisher-Yates
     permutation of [0, num_blocks) in request order, chunk order, KV-group
     order, then block order; every wave of a phase draws a fresh permutation
     (fresh, fragmented ids), or all phases share one permutation when the
-    config says so."""
+    config says so.  Phases with holes or tails also need the KV groups of
+    KDA layers, N and the chunk size (read back from a layout) to null the
+    missing entries."""
     ids_per_chunk = n_kv_groups * blocks_per_chunk
     max_chunks = num_blocks // ids_per_chunk
     waves = []
@@ -369,10 +418,28 @@ def plan_waves(cfg: Config, num_blocks: int, n_kv_groups: int, blocks_per_chunk:
                 tag = TAG_STORE_IDS if ph.op == "store" else TAG_RETRIEVE_IDS
                 flat = permutation(derive_seed(cfg.seed, tag, pi, wi), num_blocks)[:need]
             ids = flat.reshape(len(chunks), n_kv_groups, blocks_per_chunk).copy()
+            toks = None
+            if ph.snapshot_every > 1 or ph.tail_tokens:
+                if not block_tokens or not chunk_tokens:
+                    raise ValueError("holes and tails need the block and chunk sizes")
+                toks = np.full(len(chunks), chunk_tokens, dtype=np.int32)
+                for n, (r, c) in enumerate(chunks):
+                    t = ph.tail_tokens.get((r, c), chunk_tokens)
+                    toks[n] = t
+                    for j in range(blocks_per_chunk):
+                        b = c * blocks_per_chunk + j           # block index in the request
+                        complete = (j + 1) * block_tokens <= t  # block ends inside the chunk
+                        snap = complete and (b + 1) % ph.snapshot_every == 0
+                        for g in range(n_kv_groups):
+                            if g in kda_groups:
+                                if not snap:
+                                    ids[n, g, j] = NULL_BLOCK
+                            elif j * block_tokens >= t:         # MLA block past the tail
+                                ids[n, g, j] = NULL_BLOCK
             pool_seed = None
             if ph.op == "store" and not cfg.shared_permutation:
                 pool_seed = derive_seed(cfg.seed, TAG_POOL, pi, wi)
-            waves.append(Wave(ph.op, chunks, ids, pool_seed, ph.prefilled_objects))
+            waves.append(Wave(ph.op, chunks, ids, pool_seed, ph.prefilled_objects, toks))
     return waves
 
 

@@ -32,7 +32,9 @@ class GpuWorkload:
         self.layout = hkv.Layout(desc)
         info = self.layout.info
         self.info = info
-        self.waves = W.plan_waves(cfg, info["num_blocks"], self.layout.G, self.layout.k)
+        kda_groups = {L["kv_group"] for L in self.layout.layers if not L["is_mla"]}
+        self.waves = W.plan_waves(cfg, info["num_blocks"], self.layout.G, self.layout.k,
+                                  kda_groups, info["block_size"], info["chunk_tokens"])
         self.stream = stream if stream is not None else torch.cuda.Stream(device=self.device)
         # object slots
         self.slot_of = {}
@@ -108,7 +110,7 @@ class GpuWorkload:
         ptrs = self.object_ptrs(w.chunks)
         fn = self.layout.store if w.op == "store" else self.layout.retrieve
         fn(self.pool.data_ptr(), w.ids, ptrs, self.ws.data_ptr(), self.ws_bytes,
-           self.stream.cuda_stream)
+           self.stream.cuda_stream, chunk_tokens=w.chunk_tokens)
 
     def run_all(self, on_wave=None) -> None:
         """Every wave in order.  A store wave with a pool seed first refills
