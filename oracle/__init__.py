@@ -22,7 +22,7 @@ DESC_KEYS = (
     "is_mla", "kda_heads", "kda_head_dim", "kda_state_bytes", "conv_dim", "conv_kernel",
     "conv_bytes", "mla_width", "mla_bytes", "block_size", "chunk_min_tokens",
     "strict_chunk_multiple", "path", "separate_object_groups", "kv_group_of_layer",
-    "pool_bytes", "max_num_batched_tokens",
+    "pool_bytes", "max_num_batched_tokens", "kda_codec",
 )
 
 OK, E_ARG, E_COVER, E_CHUNK, E_BATCH, E_POOL, E_RANGE, E_ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
@@ -59,7 +59,7 @@ def bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.hkvref_chunk_tokens.argtypes = [i64, i64, i32, ctypes.POINTER(i64)]
     L.hkvref_layout_init.restype = ctypes.c_int
     L.hkvref_layout_init.argtypes = [i32, vp, i32, i32, i32, i32, i32, i32, i32, i32,
-                                     i64, i64, i32, i32, i32, vp, u64, i64,
+                                     i64, i64, i32, i32, i32, vp, u64, i64, i32,
                                      ctypes.POINTER(vp)]
     L.hkvref_layout_free.restype = None
     L.hkvref_layout_free.argtypes = [vp]
@@ -73,6 +73,8 @@ def bind(L: ctypes.CDLL) -> ctypes.CDLL:
     L.hkvref_retrieve_chunks.argtypes = [vp, vp, i32, vp, vp, vp]
     L.hkvref_fingerprint.restype = u64
     L.hkvref_fingerprint.argtypes = [vp]
+    L.hkvref_codec_page.restype = ctypes.c_int
+    L.hkvref_codec_page.argtypes = [vp, i32, vp, vp]
     L.hkvref_chunk_keys.restype = ctypes.c_int
     L.hkvref_chunk_keys.argtypes = [vp, vp, i64, i32, u64, u64, vp, vp, i32,
                                     ctypes.POINTER(i64)]
@@ -102,9 +104,9 @@ def chunk_tokens(n: int, chunk_min: int, strict: bool = False) -> int:
 
 SUMMARY_FIELDS = ("block_size", "chunk_tokens", "blocks_per_chunk", "num_blocks", "n_layers",
                   "n_kv_groups", "n_obj_groups", "path", "n_slabs", "unified_page_bytes",
-                  "block_stride", "obj_bytes0", "obj_bytes1", "pool_bytes_used")
+                  "block_stride", "obj_bytes0", "obj_bytes1", "pool_bytes_used", "kda_codec")
 LAYER_FIELDS = ("is_mla", "kv_group", "obj_group", "slot", "page_bytes", "reserved_bytes",
-                "pool_offset", "stride", "obj_offset")
+                "pool_offset", "stride", "obj_offset", "obj_page_bytes")
 
 
 def _ptr_array(objects, n_chunks: int, n_obj: int):
@@ -142,16 +144,17 @@ class Layout:
             int(desc.get("strict_chunk_multiple", 0)), desc["path"],
             int(desc.get("separate_object_groups", 1)),
             None if kvg_arr is None else kvg_arr.ctypes.data,
-            desc["pool_bytes"], desc.get("max_num_batched_tokens", 0), ctypes.byref(h))
+            desc["pool_bytes"], desc.get("max_num_batched_tokens", 0),
+            int(desc.get("kda_codec", 0)), ctypes.byref(h))
         if rc != OK:
             raise OracleError(rc, "layout_init")
         self._h = h
-        s = (ctypes.c_int64 * 14)()
+        s = (ctypes.c_int64 * 15)()
         L.hkvref_layout_summary(h, s)
         self.summary = dict(zip(SUMMARY_FIELDS, [int(v) for v in s]))
         self.layers = []
         for l in range(self.summary["n_layers"]):
-            o = (ctypes.c_int64 * 9)()
+            o = (ctypes.c_int64 * 10)()
             L.hkvref_layer(h, l, o)
             self.layers.append(dict(zip(LAYER_FIELDS, [int(v) for v in o])))
 
@@ -225,6 +228,24 @@ class Layout:
 
     def fingerprint(self) -> int:
         return int(self._L.hkvref_fingerprint(self._h))
+
+    def codec_page(self, page, encode=True, layer=None):
+        """One KDA page through the codec: a pool page (page bytes) to its
+        object form, or (encode=False) back."""
+        if layer is None:
+            layer = next(l for l, L in enumerate(self.layers) if not L["is_mla"])
+        L = self.layers[layer]
+        src = np.ascontiguousarray(page, dtype=np.uint8)
+        n_in, n_out = ((L["page_bytes"], L["obj_page_bytes"]) if encode
+                       else (L["obj_page_bytes"], L["page_bytes"]))
+        if src.size != n_in:
+            raise ValueError(f"expected {n_in} bytes, got {src.size}")
+        out = np.empty(n_out, np.uint8)
+        rc = self._L.hkvref_codec_page(self._h, 1 if encode else 0, src.ctypes.data,
+                                       out.ctypes.data)
+        if rc != OK:
+            raise OracleError(rc, "codec_page")
+        return out
 
     def chunk_keys(self, tokens, hash_block_tokens=0, root=0, rank_tag=0):
         """(prefix hashes [n_tokens // h], keys [n_chunks][O]) as uint64 arrays."""

@@ -9,6 +9,7 @@
  */
 #include "hkvref.h"
 
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -21,6 +22,9 @@ struct hkvref_layout {
     int64_t obj_bytes[2];
     int64_t shape[8]; /* heads, head_dim, state_bytes, conv_dim, conv_kernel, conv_bytes,
                          mla_width, mla_bytes */
+    int32_t codec;      /* 0 = opaque KDA pages; 1 = INT8 recurrent-state codec */
+    int64_t conv_part;  /* bytes of the conv state at the start of a KDA page */
+    int64_t* obj_page;  /* bytes a layer's page takes in an object */
     int32_t* is_mla;
     int32_t* kv_group;
     int32_t* obj_group;
@@ -95,6 +99,7 @@ static void layout_free_arrays(hkvref_layout* lay)
     free(lay->pool_offset);
     free(lay->stride);
     free(lay->obj_offset);
+    free(lay->obj_page);
 }
 
 void hkvref_layout_free(hkvref_layout* lay)
@@ -159,7 +164,7 @@ int hkvref_layout_init(int32_t n_layers, const uint8_t* is_mla_in,
                        int64_t block_size, int64_t chunk_min, int32_t strict,
                        int32_t path, int32_t separate_objects,
                        const int32_t* kv_group_of_layer,
-                       uint64_t pool_bytes, int64_t max_batched,
+                       uint64_t pool_bytes, int64_t max_batched, int32_t kda_codec,
                        hkvref_layout** out)
 {
     hkvref_layout* lay;
@@ -172,6 +177,16 @@ int hkvref_layout_init(int32_t n_layers, const uint8_t* is_mla_in,
         return HKVREF_E_ARG;
     if (heads < 1 || head_dim < 1 || state_bytes < 1 || conv_dim < 0 || conv_kernel < 1 ||
         conv_bytes < 1)
+        return HKVREF_E_ARG;
+    /* The INT8 codec reads the recurrent state as fp32 rows of head_dim
+     * values (16..256, a power of two) after a conv part of whole 16-byte
+     * units. */
+    if (kda_codec != 0 && kda_codec != 1)
+        return HKVREF_E_ARG;
+    if (kda_codec == 1 &&
+        (state_bytes != 4 || (head_dim != 16 && head_dim != 32 && head_dim != 64 &&
+                              head_dim != 128 && head_dim != 256) ||
+         ((int64_t)conv_dim * (conv_kernel - 1) * conv_bytes) % 16 != 0))
         return HKVREF_E_ARG;
 
     lay = (hkvref_layout*)calloc(1, sizeof(*lay));
@@ -187,6 +202,8 @@ int hkvref_layout_init(int32_t n_layers, const uint8_t* is_mla_in,
     lay->shape[5] = conv_bytes;
     lay->shape[6] = mla_width;
     lay->shape[7] = mla_bytes;
+    lay->codec = kda_codec;
+    lay->conv_part = (int64_t)conv_dim * (conv_kernel - 1) * conv_bytes;
     lay->is_mla = (int32_t*)calloc((size_t)n_layers, sizeof(int32_t));
     lay->kv_group = (int32_t*)calloc((size_t)n_layers, sizeof(int32_t));
     lay->obj_group = (int32_t*)calloc((size_t)n_layers, sizeof(int32_t));
@@ -196,8 +213,10 @@ int hkvref_layout_init(int32_t n_layers, const uint8_t* is_mla_in,
     lay->pool_offset = (int64_t*)calloc((size_t)n_layers, sizeof(int64_t));
     lay->stride = (int64_t*)calloc((size_t)n_layers, sizeof(int64_t));
     lay->obj_offset = (int64_t*)calloc((size_t)n_layers, sizeof(int64_t));
+    lay->obj_page = (int64_t*)calloc((size_t)n_layers, sizeof(int64_t));
     if (!lay->is_mla || !lay->kv_group || !lay->obj_group || !lay->index_in_group ||
-        !lay->page || !lay->reserved || !lay->pool_offset || !lay->stride || !lay->obj_offset) {
+        !lay->page || !lay->reserved || !lay->pool_offset || !lay->stride || !lay->obj_offset ||
+        !lay->obj_page) {
         hkvref_layout_free(lay);
         return HKVREF_E_ARG;
     }
@@ -365,20 +384,29 @@ int hkvref_layout_init(int32_t n_layers, const uint8_t* is_mla_in,
             lay->obj_group[l] = 0;
     }
     /* Object byte layout (reading): layer-major in model order, then the k
-     * blocks of the chunk, real page bytes only, no header. */
+     * blocks of the chunk, real page bytes only, no header.  With the codec
+     * a KDA page takes conv part + rows x head_dim codes + rows x 4 scale
+     * bytes (rows = heads x head_dim). */
+    for (l = 0; l < n_layers; l++) {
+        int64_t rows = (int64_t)heads * head_dim;
+        if (kda_codec == 1 && !lay->is_mla[l])
+            lay->obj_page[l] = lay->conv_part + rows * head_dim + rows * 4;
+        else
+            lay->obj_page[l] = lay->page[l];
+    }
     for (o = 0; o < 2; o++)
         lay->obj_bytes[o] = 0;
     for (l = 0; l < n_layers; l++) {
         o = lay->obj_group[l];
         lay->obj_offset[l] = lay->obj_bytes[o];
-        lay->obj_bytes[o] += lay->k * lay->page[l];
+        lay->obj_bytes[o] += lay->k * lay->obj_page[l];
     }
 
     *out = lay;
     return HKVREF_OK;
 }
 
-int hkvref_layout_summary(const hkvref_layout* lay, int64_t out[14])
+int hkvref_layout_summary(const hkvref_layout* lay, int64_t out[15])
 {
     if (lay == NULL || out == NULL)
         return HKVREF_E_ARG;
@@ -396,10 +424,11 @@ int hkvref_layout_summary(const hkvref_layout* lay, int64_t out[14])
     out[11] = lay->obj_bytes[0];
     out[12] = lay->n_obj_groups > 1 ? lay->obj_bytes[1] : 0;
     out[13] = lay->addressed_bytes;
+    out[14] = lay->codec;
     return HKVREF_OK;
 }
 
-int hkvref_layer(const hkvref_layout* lay, int32_t layer, int64_t out[9])
+int hkvref_layer(const hkvref_layout* lay, int32_t layer, int64_t out[10])
 {
     if (lay == NULL || out == NULL || layer < 0 || layer >= lay->n_layers)
         return HKVREF_E_ARG;
@@ -412,6 +441,7 @@ int hkvref_layer(const hkvref_layout* lay, int32_t layer, int64_t out[9])
     out[6] = lay->pool_offset[layer];
     out[7] = lay->stride[layer];
     out[8] = lay->obj_offset[layer];
+    out[9] = lay->obj_page[layer];
     return HKVREF_OK;
 }
 
@@ -473,6 +503,102 @@ static int64_t valid_bytes(const hkvref_layout* lay, int32_t l, int64_t j, int64
     return rows * (lay->page[l] / lay->n);
 }
 
+/* INT8 codec of the KDA recurrent state (Mooncake K3 blog, Compressed
+ * Checkpoint Storage: inactive recurrent states are compressed to INT8 with
+ * per-channel quantization parameters while the conv window keeps its
+ * precision).  Readings: a channel is one row of head_dim values of the
+ * (heads, d, d) state; s = (largest finite |x| of the row) / 127 in fp32;
+ * q = round-half-even(x / s) clamped to [-127, 127]; non-finite x and rows
+ * with s == 0 give q = 0; decoding gives q * s. */
+static void encode_row(const float* x, int64_t d, int8_t* q, float* scale)
+{
+    float amax = 0.0f, s, v;
+    int64_t i;
+    for (i = 0; i < d; i++)
+        if (isfinite(x[i]) && fabsf(x[i]) > amax)
+            amax = fabsf(x[i]);
+    s = amax / 127.0f;
+    *scale = s;
+    for (i = 0; i < d; i++) {
+        if (s == 0.0f || !isfinite(x[i])) {
+            q[i] = 0;
+            continue;
+        }
+        v = rintf(x[i] / s);
+        if (v > 127.0f)
+            v = 127.0f;
+        if (v < -127.0f)
+            v = -127.0f;
+        q[i] = (int8_t)v;
+    }
+}
+
+/* Decoding is one fp32 product per value.  An object the encoder did not
+ * write (a non-finite scale, code -128) can make it NaN; such a NaN is
+ * written as the default quiet NaN 0x7FC00000, so the bytes do not depend on
+ * which operand's payload a machine propagates. */
+static void decode_row(const int8_t* q, float scale, int64_t d, float* x)
+{
+    const uint32_t qnan = 0x7FC00000u;
+    int64_t i;
+    for (i = 0; i < d; i++) {
+        x[i] = (float)q[i] * scale;
+        if (isnan(x[i]))
+            memcpy(&x[i], &qnan, 4);
+    }
+}
+
+/* A KDA page in codec form: the conv part verbatim, then the codes of every
+ * row, then every row's scale.  The page is the conv state followed by the
+ * recurrent state (the order of the two state shapes in vLLM hybrid KV-cache
+ * blog, section 2.1). */
+static void encode_page(const hkvref_layout* lay, const uint8_t* page, uint8_t* out)
+{
+    int64_t d = lay->shape[1], rows = lay->shape[0] * lay->shape[1], r;
+    uint8_t* codes = out + lay->conv_part;
+    uint8_t* scales = codes + rows * d;
+    float* x = (float*)malloc((size_t)d * sizeof(float));
+    int8_t* q = (int8_t*)malloc((size_t)d);
+    memcpy(out, page, (size_t)lay->conv_part);
+    for (r = 0; r < rows; r++) {
+        float sc;
+        memcpy(x, page + lay->conv_part + r * d * 4, (size_t)d * 4);
+        encode_row(x, d, q, &sc);
+        memcpy(codes + r * d, q, (size_t)d);
+        memcpy(scales + r * 4, &sc, 4);
+    }
+    free(x);
+    free(q);
+}
+
+static void decode_page(const hkvref_layout* lay, const uint8_t* in, uint8_t* page)
+{
+    int64_t d = lay->shape[1], rows = lay->shape[0] * lay->shape[1], r;
+    const uint8_t* codes = in + lay->conv_part;
+    const uint8_t* scales = codes + rows * d;
+    float* x = (float*)malloc((size_t)d * sizeof(float));
+    memcpy(page, in, (size_t)lay->conv_part);
+    for (r = 0; r < rows; r++) {
+        float sc;
+        memcpy(&sc, scales + r * 4, 4);
+        decode_row((const int8_t*)(codes + r * d), sc, d, x);
+        memcpy(page + lay->conv_part + r * d * 4, x, (size_t)d * 4);
+    }
+    free(x);
+}
+
+int hkvref_codec_page(const hkvref_layout* lay, int32_t encode, const uint8_t* in,
+                      uint8_t* out)
+{
+    if (lay == NULL || in == NULL || out == NULL || lay->codec != 1)
+        return HKVREF_E_ARG;
+    if (encode)
+        encode_page(lay, in, out);
+    else
+        decode_page(lay, in, out);
+    return HKVREF_OK;
+}
+
 /* Store: gather each chunk's pages out of the paged pool into its objects.
  * A page is copied as opaque bytes ("Kimi-Linear" recipe: LMCache treats the
  * KDA state as an opaque page; Caveats: the pages are byte-opaque).  Object
@@ -501,10 +627,14 @@ int hkvref_store_chunks(const hkvref_layout* lay, const uint8_t* pool,
             uint8_t* obj = objects[(int64_t)c * lay->n_obj_groups + lay->obj_group[l]];
             for (j = 0; j < lay->k; j++) {
                 int64_t id = block_id(lay, block_ids, c, lay->kv_group[l], j);
-                uint8_t* dst = obj + lay->obj_offset[l] + j * lay->page[l];
+                uint8_t* dst = obj + lay->obj_offset[l] + j * lay->obj_page[l];
                 int64_t v;
                 if (id == HKVREF_NULL_BLOCK) {
-                    memset(dst, 0, (size_t)lay->page[l]);
+                    memset(dst, 0, (size_t)lay->obj_page[l]);
+                    continue;
+                }
+                if (lay->codec && !lay->is_mla[l]) {
+                    encode_page(lay, pool + lay->pool_offset[l] + id * lay->stride[l], dst);
                     continue;
                 }
                 v = valid_bytes(lay, l, j, t);
@@ -544,8 +674,13 @@ int hkvref_retrieve_chunks(const hkvref_layout* lay, uint8_t* pool,
                 int64_t id = block_id(lay, block_ids, c, lay->kv_group[l], j);
                 if (id == HKVREF_NULL_BLOCK)
                     continue;
+                if (lay->codec && !lay->is_mla[l]) {
+                    decode_page(lay, obj + lay->obj_offset[l] + j * lay->obj_page[l],
+                                pool + lay->pool_offset[l] + id * lay->stride[l]);
+                    continue;
+                }
                 memcpy(pool + lay->pool_offset[l] + id * lay->stride[l],
-                       obj + lay->obj_offset[l] + j * lay->page[l],
+                       obj + lay->obj_offset[l] + j * lay->obj_page[l],
                        (size_t)valid_bytes(lay, l, j, t));
             }
         }
@@ -584,11 +719,12 @@ uint64_t hkvref_fingerprint(const hkvref_layout* lay)
     for (i = 0; i < 8; i++)
         words[n++] = (uint64_t)lay->shape[i];
     words[n++] = (uint64_t)lay->n_obj_groups;
+    words[n++] = (uint64_t)lay->codec;
     for (i = 0; i < n; i++)
         f = ref_mix64(f ^ words[i]);
     for (l = 0; l < lay->n_layers; l++) {
         uint64_t w = (uint64_t)lay->is_mla[l] | ((uint64_t)lay->obj_group[l] << 1) |
-                     ((uint64_t)lay->page[l] << 8);
+                     ((uint64_t)lay->obj_page[l] << 8);
         f = ref_mix64(f ^ w);
     }
     return f;

@@ -18,6 +18,8 @@
  *     per-layer offset + shared block stride): vLLM hybrid KV-cache blog,
  *     sections 3.1 and 3.2;
  *   - object groups: "Hybrid Attention Models", Object-group separation;
+ *   - the optional INT8 codec of inactive KDA states: Mooncake K3 blog,
+ *     Compressed Checkpoint Storage;
  *   - store/retrieve: one memcpy per (chunk, layer, block) page.
  *
  * Every function returns 0 on success or a negative status code (the same
@@ -65,7 +67,7 @@ int hkvref_layout_init(int32_t n_layers, const uint8_t* is_mla,
                        int64_t block_size, int64_t chunk_min, int32_t strict,
                        int32_t path, int32_t separate_objects,
                        const int32_t* kv_group_of_layer,
-                       uint64_t pool_bytes, int64_t max_batched,
+                       uint64_t pool_bytes, int64_t max_batched, int32_t kda_codec,
                        hkvref_layout** out);
 void hkvref_layout_free(hkvref_layout* lay);
 
@@ -73,14 +75,15 @@ void hkvref_layout_free(hkvref_layout* lay);
  * [5]=G (KV groups), [6]=O (object groups), [7]=path, [8]=slabs (path A),
  * [9]=unified page P (path A, else 0), [10]=block stride (path B, else P),
  * [11]=obj_bytes[0], [12]=obj_bytes[1] (0 if O==1), [13]=bytes of the pool
- * the layout addresses. */
-int hkvref_layout_summary(const hkvref_layout* lay, int64_t out[14]);
+ * the layout addresses, [14]=KDA codec (0 none, 1 INT8). */
+int hkvref_layout_summary(const hkvref_layout* lay, int64_t out[15]);
 
 /* Per layer: out[0]=is_mla, [1]=kv_group, [2]=obj_group, [3]=slab / index in
  * group, [4]=real page bytes, [5]=bytes reserved for it per block,
  * [6]=pool offset of block 0's page, [7]=stride between block ids,
- * [8]=offset of its block-0 page inside its object. */
-int hkvref_layer(const hkvref_layout* lay, int32_t layer, int64_t out[9]);
+ * [8]=offset of its block-0 page inside its object, [9]=bytes its page
+ * takes in an object (the INT8 form for KDA layers under the codec). */
+int hkvref_layer(const hkvref_layout* lay, int32_t layer, int64_t out[10]);
 
 /* A block id that names no page: a missing KDA snapshot, or an MLA block
  * past a partial chunk's last token. */
@@ -102,10 +105,17 @@ int hkvref_retrieve_chunks(const hkvref_layout* lay, uint8_t* pool,
                            int32_t n_chunks, const int32_t* block_ids,
                            const int32_t* chunk_tokens, const uint8_t* const* objects);
 
+/* The codec on one KDA page: encode = 1 turns a pool page (the layout's
+ * page bytes) into its object form (object page bytes); encode = 0 the
+ * reverse.  HKVREF_E_ARG if the layout has no codec. */
+int hkvref_codec_page(const hkvref_layout* lay, int32_t encode, const uint8_t* in,
+                      uint8_t* out);
+
 /* Object-format fingerprint: mix64-fold (f = mix64(f ^ w), f0 = GAMMA) of
  * 1, N, k, n_layers, the eight per-rank shapes (heads, head_dim,
  * state_bytes, conv_dim, conv_kernel, conv_bytes, mla_width, mla_bytes),
- * n_obj_groups, then per layer is_mla | obj_group << 1 | page << 8. */
+ * n_obj_groups, codec, then per layer is_mla | obj_group << 1 |
+ * object page bytes << 8. */
 uint64_t hkvref_fingerprint(const hkvref_layout* lay);
 
 /* Chained prefix hashes over hash blocks of h tokens (h divides N; 0 = N)

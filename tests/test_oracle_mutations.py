@@ -1,6 +1,6 @@
 """The pins catch plausible mistakes in the oracle.
 
-Each case plants one mistake in a copy of oracle/hkvref.c (on the CPU), builds
+Each case plants one mistake (one or more consistent edits) in a copy of oracle/hkvref.c (on the CPU), builds
 it, points the oracle wrapper at it, and runs the pins of
 test_oracle_pins.py until one fails.  A mutant that passes every pin would
 mean the pins do not fix that part of the oracle.
@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 from tests import golden_io
+from tests import test_codec as codec
 from tests import test_keys as keys
 from tests import test_oracle_pins as pins
 
@@ -30,7 +31,7 @@ MUTANTS = {
         "                byte_offset += lay->page[l];\n"
         "                lay->pool_offset[l] = byte_offset - lay->page[0];"),
     "object_block_offset_uses_stride": (
-        "uint8_t* dst = obj + lay->obj_offset[l] + j * lay->page[l];",
+        "uint8_t* dst = obj + lay->obj_offset[l] + j * lay->obj_page[l];",
         "uint8_t* dst = obj + lay->obj_offset[l] + j * lay->stride[l] % 64;"),
     "block_table_index_transposed": (
         "return ids[((int64_t)c * lay->n_kv_groups + g) * lay->k + j];",
@@ -50,7 +51,7 @@ MUTANTS = {
         "                       (size_t)valid_bytes(lay, l, j, t));",
         "                       (size_t)lay->page[l]);"),
     "null_page_not_zeroed_on_store": (
-        "                    memset(dst, 0, (size_t)lay->page[l]);\n                    continue;",
+        "                    memset(dst, 0, (size_t)lay->obj_page[l]);\n                    continue;",
         "                    continue;"),
     "partial_rows_counted_from_block_start": (
         "    rows = t - j * lay->n;",
@@ -95,6 +96,60 @@ MUTANTS = {
     "conv_state_keeps_kernel_columns": (
         "int64_t conv = (int64_t)conv_dim * (conv_kernel - 1) * conv_bytes;",
         "int64_t conv = (int64_t)conv_dim * conv_kernel * conv_bytes;"),
+    # the INT8 codec of KDA recurrent states
+    "codec_scale_over_128": (
+        "    s = amax / 127.0f;",
+        "    s = amax / 128.0f;"),
+    "codec_truncates": (
+        "        v = rintf(x[i] / s);",
+        "        v = truncf(x[i] / s);"),
+    "codec_rounds_half_away": (
+        "        v = rintf(x[i] / s);",
+        "        v = roundf(x[i] / s);"),
+    "codec_absmax_sees_non_finite": (
+        "        if (isfinite(x[i]) && fabsf(x[i]) > amax)",
+        "        if (fabsf(x[i]) > amax && !isnan(x[i]))"),
+    "codec_encodes_non_finite": (
+        "        if (s == 0.0f || !isfinite(x[i])) {",
+        "        if (s == 0.0f) {"),
+    "codec_absmax_signed": (
+        "        if (isfinite(x[i]) && fabsf(x[i]) > amax)\n            amax = fabsf(x[i]);",
+        "        if (isfinite(x[i]) && x[i] > amax)\n            amax = x[i];"),
+    "codec_scales_before_codes": [
+        ("    uint8_t* codes = out + lay->conv_part;\n    uint8_t* scales = codes + rows * d;",
+         "    uint8_t* scales = out + lay->conv_part;\n    uint8_t* codes = scales + rows * 4;"),
+        ("    const uint8_t* codes = in + lay->conv_part;\n"
+         "    const uint8_t* scales = codes + rows * d;",
+         "    const uint8_t* scales = in + lay->conv_part;\n"
+         "    const uint8_t* codes = scales + rows * 4;")],
+    "codec_state_before_conv": [
+        ("memcpy(x, page + lay->conv_part + r * d * 4, (size_t)d * 4);",
+         "memcpy(x, page + r * d * 4, (size_t)d * 4);"),
+        ("memcpy(page + lay->conv_part + r * d * 4, x, (size_t)d * 4);",
+         "memcpy(page + r * d * 4, x, (size_t)d * 4);"),
+        ("    memcpy(out, page, (size_t)lay->conv_part);",
+         "    memcpy(out, page + rows * d * 4, (size_t)lay->conv_part);"),
+        ("    memcpy(page, in, (size_t)lay->conv_part);",
+         "    memcpy(page + rows * d * 4, in, (size_t)lay->conv_part);")],
+    "codec_decode_keeps_nan_payloads": (
+        "        if (isnan(x[i]))\n            memcpy(&x[i], &qnan, 4);",
+        ""),
+    "codec_decode_clamps_codes": (
+        "        x[i] = (float)q[i] * scale;",
+        "        x[i] = (float)(q[i] < -127 ? -127 : q[i]) * scale;"),
+    "codec_drops_conv_part": (
+        "    memcpy(out, page, (size_t)lay->conv_part);",
+        "    memset(out, 0, (size_t)lay->conv_part);"),
+    "codec_one_scale_per_page": (
+        "        memcpy(&sc, scales + r * 4, 4);",
+        "        memcpy(&sc, scales, 4);"),
+    "codec_rows_per_head_only": (
+        "            lay->obj_page[l] = lay->conv_part + rows * head_dim + rows * 4;",
+        "            lay->obj_page[l] = lay->conv_part + heads * head_dim + heads * 4;"),
+    "codec_accepts_any_head_dim": (
+        "        (state_bytes != 4 || (head_dim != 16 && head_dim != 32 && head_dim != 64 &&\n"
+        "                              head_dim != 128 && head_dim != 256) ||",
+        "        (state_bytes != 4 ||"),
 }
 
 
@@ -120,6 +175,13 @@ def pin_checks():
         out.append(lambda c=case: pins.test_brute_force_every_injective_assignment(c))
     out += [pins.test_id_range_and_alias_errors, pins.test_whole_chunks_and_no_nulls_reduce_to_plain_copies,
             pins.test_random_layouts_store_retrieve_properties, pins.test_null_ids_and_partial_chunks]
+    out += [codec.test_object_page_is_conv_then_codes_then_scales,
+            codec.test_ties_round_half_to_even, codec.test_zero_and_non_finite_rows,
+            codec.test_power_of_two_lattice_round_trips_exactly, codec.test_denormal_rows,
+            codec.test_null_pages_and_mla_pages_under_the_codec,
+            codec.test_codec_changes_the_fingerprint_and_rejects_unsupported_shapes,
+            codec.test_decode_of_objects_the_encoder_did_not_write,
+            codec.test_round_off_bound_and_extremal_code]
     out += [keys.test_fine_hash_covers_exactly_its_prefix,
             keys.test_chunk_hash_is_its_last_fine_block_hash,
             keys.test_chain_continues_from_a_parent, keys.test_hash_depends_on_token_order_within_a_block,
@@ -135,21 +197,23 @@ def run_pins_against(lib_path: str) -> int:
     for check in pin_checks():
         try:
             check()
-        except (AssertionError, oracle.OracleError):
+        except (AssertionError, oracle.OracleError, pytest.fail.Exception):
             return 1
     return 0
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name, tmp_path):
-    original, planted = MUTANTS[name]
+    edits = MUTANTS[name]
     src = open(SRC).read()
-    assert src.count(original) == 1, "the mutation site moved; update the test"
+    for original, planted in (edits if isinstance(edits, list) else [edits]):
+        assert src.count(original) == 1, "the mutation site moved; update the test"
+        src = src.replace(original, planted)
     mutant = tmp_path / "hkvref.c"
-    mutant.write_text(src.replace(original, planted))
+    mutant.write_text(src)
     (tmp_path / "hkvref.h").write_text(open(SRC[:-1] + "h").read())
     so = tmp_path / "libmut.so"
-    subprocess.run(["gcc", "-O1", "-w", "-fPIC", "-shared", str(mutant), "-o", str(so)],
+    subprocess.run(["gcc", "-O1", "-w", "-fPIC", "-shared", str(mutant), "-o", str(so), "-lm"],
                    check=True)
     # a child process: a mutant may also crash (e.g. divide by zero), which
     # counts as caught
