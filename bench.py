@@ -23,7 +23,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 HOST_LINK_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction (32 GT/s x 16 lanes, 128b/130b)
 METRIC = "store+retrieve GB/s of KV/state pages (Kimi-Linear shapes, N=1888); % HBM peak"
-COPY_SRC = os.path.join(ROOT, "retrieve_store_chunk_amd", "csrc", "hkv_copy.hip")
+CSRC = os.path.join(ROOT, "retrieve_store_chunk_amd", "csrc")
+KERNEL_SOURCES = ("hkv_copy.hip", "hkv_device_tables.hpp", "hkv_launch.hpp", "hkv_plan.cpp")
 
 
 def log(msg: str) -> None:
@@ -31,8 +32,14 @@ def log(msg: str) -> None:
 
 
 def kernel_source_sha() -> str:
-    with open(COPY_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the sources that decide what the copy kernels do per launch:
+    the kernels, their shared tables and launch header, and the planner that
+    lays out the work items."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(config: str, tile: int, max_wg: int):
@@ -51,15 +58,17 @@ def load_traffic(config: str, tile: int, max_wg: int):
 
 
 def wave_bytes(layout, w) -> tuple:
-    """(data bytes, object bytes) of one call.  Data bytes are page bytes that
-    hold data: every real byte of a page, none for a null id, and for an MLA
-    page of a partial chunk the rows of its valid tokens.  Object bytes are
-    the chunks' whole objects (a store writes all of them; what has no data
-    behind it is zero-filled)."""
+    """(data bytes, object bytes, live object bytes) of one call.  Data bytes
+    are pool page bytes that hold data: every real byte of a page, none for a
+    null id, and for an MLA page of a partial chunk the rows of its valid
+    tokens.  Object bytes are the chunks' whole objects (a store writes all of
+    them; what has no data behind it is zero-filled).  Live object bytes are
+    the object bytes behind the data bytes: the same count, except for KDA
+    pages in INT8 form, which take their smaller object page size."""
     import numpy as np
     info = layout.info
     N, k, n = info["block_size"], info["blocks_per_chunk"], len(w.chunks)
-    data = 0
+    data = live = 0
     for L in layout.layers:
         present = w.ids[:, L["kv_group"], :] != -1
         if L["is_mla"] and w.chunk_tokens is not None:
@@ -68,11 +77,15 @@ def wave_bytes(layout, w) -> tuple:
         else:
             per = np.full((n, k), L["page_bytes"], dtype=np.int64)
         data += int((per * present).sum())
-    return data, n * info["chunk_payload_bytes"]
+        if L["obj_page_bytes"] != L["page_bytes"]:
+            per = np.full((n, k), L["obj_page_bytes"], dtype=np.int64)
+        live += int((per * present).sum())
+    return data, n * info["chunk_payload_bytes"], live
 
 
 def cpu_baseline(cfg, min_seconds: float = 10.0, max_seconds: float = 30.0) -> dict:
-    """The oracle (plain C, one thread, one memcpy per page) on a bounded
+    """The oracle (plain C, one thread, one memcpy per page, or its INT8 codec
+    loop for KDA pages when the layout has one) on a bounded
     sample of the same workload: the same layout shapes in a smaller pool,
     64 chunks stored and their first halves retrieved into fresh ids,
     repeated until at least min_seconds of CPU time."""
@@ -96,7 +109,8 @@ def cpu_baseline(cfg, min_seconds: float = 10.0, max_seconds: float = 30.0) -> d
     perm2 = W.permutation(W.derive_seed(cfg.seed, 1235), s["num_blocks"])
     n_ret = n_store // 2
     ret_ids = perm2[: n_ret * ids_per_chunk].reshape(n_ret, lay.G, lay.k)
-    payload = (n_store + n_ret) * (s["obj_bytes0"] + s["obj_bytes1"])
+    # pool page bytes per chunk (the objects' size, unless KDA pages are INT8)
+    payload = (n_store + n_ret) * lay.k * sum(L["page_bytes"] for L in lay.layers)
     passes, t_cpu = 0, 0.0
     while t_cpu < min_seconds and (passes == 0 or t_cpu + t_cpu / passes < max_seconds):
         c0 = time.perf_counter()
@@ -109,7 +123,8 @@ def cpu_baseline(cfg, min_seconds: float = 10.0, max_seconds: float = 30.0) -> d
             "sample": f"{passes} passes of: store {n_store} chunks + retrieve {n_ret} chunks "
                       f"(same page shapes, pool of {s['num_blocks']} blocks); "
                       f"{passes * payload / 1e9:.1f} GB moved in {t_cpu:.1f} s wall, "
-                      "single-threaded plain C memcpy"}
+                      "single-threaded plain C memcpy"
+                      + (" + per-row INT8 codec of KDA pages" if s["kda_codec"] else "")}
 
 
 def hbm_ceiling(buf, stream, reps: int = 10) -> dict:
@@ -199,7 +214,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="kl_tp1",
                     help="workload: tiny, kl_tp2, kl_tp1 (default), k3_tp8, long_ctx, "
-                         "kl_tp1_host (objects in pinned host memory)")
+                         "kl_tp1_host (objects in pinned host memory), k3_tp8_holes, "
+                         "kl_tp1_tails, kl_tp1_int8 (INT8 KDA objects)")
     ap.add_argument("--tile-bytes", type=int, default=0)
     ap.add_argument("--max-workgroups", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -244,19 +260,17 @@ def main() -> int:
     stream = g.stream
     n_w = len(g.waves)
     on_host = objects_on == "host"
-    # payload = page bytes that hold data; HBM traffic: a store reads the data
-    # and writes whole objects, a retrieve reads and writes the data; with host
-    # objects the object side crosses the host link instead of HBM
+    # payload = pool page bytes that hold data; HBM traffic: a store reads the
+    # data and writes whole objects, a retrieve reads the live object bytes
+    # and writes the data; with host objects the object side crosses the host
+    # link instead of HBM
     per_wave_payload, per_wave_hbm, per_wave_link = [], [], []
     for w in g.waves:
-        data, objb = wave_bytes(g.layout, w)
+        data, objb, live = wave_bytes(g.layout, w)
         per_wave_payload.append(data)
-        if w.op == "store":
-            per_wave_hbm.append(data if on_host else data + objb)
-            per_wave_link.append(objb if on_host else 0)
-        else:
-            per_wave_hbm.append(data if on_host else 2 * data)
-            per_wave_link.append(data if on_host else 0)
+        obj_side = objb if w.op == "store" else live
+        per_wave_hbm.append(data if on_host else data + obj_side)
+        per_wave_link.append(obj_side if on_host else 0)
     step_payload = sum(per_wave_payload)
     step_hbm = sum(per_wave_hbm)
 
@@ -336,7 +350,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u8",
+        "dtype": "f32" if info.get("kda_codec") else "u8",
         "data": "synthetic",
         "config": {"workload": cfg.name, "title": cfg.title,
                    "chunks_per_step": sum(len(w.chunks) for w in g.waves),

@@ -115,6 +115,22 @@ typedef struct hkv_layout_desc {
   uint32_t max_workgroups;    /* 0 = one workgroup per tile; else the grid is capped at
                                  this many workgroups, each looping over tiles.  A
                                  tuning knob: results do not depend on it */
+  int32_t kda_codec;          /* 0 = KDA pages are stored as opaque bytes (default);
+                                 1 = INT8 codec of the recurrent state in objects, for
+                                 inactive checkpoints (Mooncake K3 blog, Compressed
+                                 Checkpoint Storage: per-channel INT8 for the recurrent
+                                 state, the conv window at full precision).  A KDA page
+                                 is read as the conv state (conv_dim x (kernel-1) x
+                                 conv_bytes, a multiple of 16 bytes) followed by the fp32
+                                 recurrent state (heads x d x d, d in {16, 32, 64, 128,
+                                 256}); in an object it becomes the conv bytes verbatim,
+                                 then int8 codes of every row of d values, then one fp32
+                                 scale per row.  Per row: s = (largest finite |x|) / 127;
+                                 q = round-half-even(x / s) clamped to [-127, 127], and 0
+                                 for non-finite x or s == 0 (x / s an IEEE fp32 division);
+                                 retrieve writes q * s in fp32, a NaN product (only from an
+                                 object the encoder did not write) as 0x7FC00000.  Lossy:
+                                 |x - q s| <= s / 2 for finite x.  Else HKV_E_ARG */
 } hkv_layout_desc;
 
 typedef struct hkv_layout hkv_layout; /* opaque; immutable after init; may be shared by
@@ -153,6 +169,7 @@ typedef struct hkv_layout_info {
   uint64_t obj_bytes[2];     /* bytes of one chunk's object of each object group (0 if
                                 unused) */
   uint64_t chunk_payload_bytes; /* obj_bytes[0] + obj_bytes[1]: bytes moved per chunk */
+  int32_t kda_codec;         /* as in hkv_layout_desc */
 } hkv_layout_info;
 
 /* Copies the layout's summary.  Errors: HKV_E_ARG. */
@@ -168,7 +185,9 @@ typedef struct hkv_layer_info {
   uint64_t pool_offset;      /* byte offset of block 0's page in the pool */
   uint64_t stride;           /* bytes between the pages of consecutive block ids */
   uint64_t obj_offset;       /* byte offset of block j=0's page inside its object; block j
-                                sits at obj_offset + j * page_bytes */
+                                sits at obj_offset + j * obj_page_bytes */
+  uint64_t obj_page_bytes;   /* bytes one page takes in an object: page_bytes, or the INT8
+                                form of a KDA page under the codec */
 } hkv_layer_info;
 
 /* Copies one layer's placement.  Errors: HKV_E_ARG (bad layer index). */
@@ -258,8 +277,8 @@ hkv_status hkv_retrieve_chunks(const hkv_layout* layout, void* pool,
  * bytes of an object would mean something else, and only then.  It folds,
  * with f = mix64(f ^ w) from f = GAMMA, the words: 1 (format version), N,
  * k, n_layers, kda_heads, kda_head_dim, kda_state_bytes, conv_dim,
- * conv_kernel, conv_bytes, mla_width, mla_bytes, n_obj_groups, and per layer
- * in model order is_mla | obj_group << 1 | page_bytes << 8.  The pool path,
+ * conv_kernel, conv_bytes, mla_width, mla_bytes, n_obj_groups, kda_codec, and
+ * per layer in model order is_mla | obj_group << 1 | obj_page_bytes << 8.  The pool path,
  * pool size, KV grouping and tuning knobs do not enter it: they do not change
  * object bytes, so objects stored from a path A pool can be retrieved into a
  * path B pool of the same model.  Errors: HKV_E_ARG. */

@@ -14,7 +14,7 @@ def build(verbose: bool = False) -> str:
     src = os.path.join(HERE, "hkvref.c")
     tmp = LIB + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror", "-fPIC", "-shared",
-           src, "-o", tmp]
+           src, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -46,7 +46,7 @@ class hkv_layout_desc(ctypes.Structure):
                 ("strict_chunk_multiple", i32), ("path", i32),
                 ("separate_object_groups", i32), ("kv_group_of_layer", ctypes.POINTER(i32)),
                 ("pool_bytes", u64), ("max_num_batched_tokens", i64), ("tile_bytes", u64),
-                ("max_workgroups", u32)]
+                ("max_workgroups", u32), ("kda_codec", i32)]
 
 
 class hkv_layout_info(ctypes.Structure):
@@ -54,13 +54,13 @@ class hkv_layout_info(ctypes.Structure):
                 ("n_layers", i32), ("n_kv_groups", i32), ("n_obj_groups", i32),
                 ("num_blocks", i64), ("path", i32), ("n_slabs", i32),
                 ("unified_page_bytes", u64), ("block_stride", u64), ("pool_bytes_used", u64),
-                ("obj_bytes", u64 * 2), ("chunk_payload_bytes", u64)]
+                ("obj_bytes", u64 * 2), ("chunk_payload_bytes", u64), ("kda_codec", i32)]
 
 
 class hkv_layer_info(ctypes.Structure):
     _fields_ = [("is_mla", i32), ("kv_group", i32), ("obj_group", i32), ("slot", i32),
                 ("page_bytes", u64), ("reserved_bytes", u64), ("pool_offset", u64),
-                ("stride", u64), ("obj_offset", u64)]
+                ("stride", u64), ("obj_offset", u64), ("obj_page_bytes", u64)]
 
 
 HKV_NULL_BLOCK = -1
@@ -176,6 +176,7 @@ def hkv_layout_init(desc: dict) -> int:
     d.max_num_batched_tokens = desc.get("max_num_batched_tokens", 0)
     d.tile_bytes = desc.get("tile_bytes", 0)
     d.max_workgroups = desc.get("max_workgroups", 0)
+    d.kda_codec = int(desc.get("kda_codec", 0))
     h = vp()
     _check(lib.hkv_layout_init(ctypes.byref(d), ctypes.byref(h)), "hkv_layout_init")
     return h.value

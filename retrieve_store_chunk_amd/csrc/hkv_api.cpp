@@ -225,6 +225,7 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   a.total_items = n * per_chunk;
   a.block_tokens = (uint64_t)p.block_size;
   a.tile_bytes = p.tile_bytes;
+  a.codec_rows_per_item = p.codec_rows_per_item;
   a.items_per_chunk = (uint32_t)per_chunk;
   a.n_kv_groups = (uint32_t)G;
   a.blocks_per_chunk = (uint32_t)k;
@@ -286,6 +287,7 @@ hkv_status hkv_layout_info_get(const hkv_layout* layout, hkv_layout_info* out) {
   out->obj_bytes[0] = p.obj_bytes[0];
   out->obj_bytes[1] = p.obj_bytes[1];
   out->chunk_payload_bytes = p.obj_bytes[0] + p.obj_bytes[1];
+  out->kda_codec = p.kda_codec;
   return HKV_OK;
 }
 
@@ -304,6 +306,7 @@ hkv_status hkv_layer_info_get(const hkv_layout* layout, int32_t layer, hkv_layer
   out->pool_offset = x.pool_offset;
   out->stride = x.stride;
   out->obj_offset = x.obj_offset;
+  out->obj_page_bytes = x.obj_page;
   return HKV_OK;
 }
 

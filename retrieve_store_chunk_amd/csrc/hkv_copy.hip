@@ -47,6 +47,17 @@ namespace {
 #ifndef HKV_XCD_REMAP
 #define HKV_XCD_REMAP 1   // give each XCD a contiguous range of work items
 #endif
+#ifndef HKV_CODEC_NT
+#define HKV_CODEC_NT 1    // nontemporal code / scale accesses in the codec
+#endif
+#ifndef HKV_WAVES_PER_EU
+#define HKV_WAVES_PER_EU 0  // waves per SIMD the register budget must allow (0: any)
+#endif
+#if HKV_WAVES_PER_EU > 0
+#define HKV_OCCUPANCY __attribute__((amdgpu_waves_per_eu(HKV_WAVES_PER_EU)))
+#else
+#define HKV_OCCUPANCY
+#endif
 
 constexpr uint32_t kThreads = hkv::kCopyThreads;
 constexpr uint32_t kUnroll = HKV_UNROLL;
@@ -111,6 +122,148 @@ __device__ __forceinline__ void zero_span(uint8_t* dst, uint32_t bytes) {
   }
 }
 
+__device__ __forceinline__ uint32_t load4(const HKV_GLOBAL uint32_t* p) {
+#if HKV_CODEC_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+__device__ __forceinline__ void store4(HKV_GLOBAL uint32_t* p, uint32_t v) {
+#if HKV_CODEC_NT
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
+__device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_uint(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// One decoded value: the low code byte times the row scale, with a NaN
+// (possible only for an object the encoder did not write) written as the
+// default quiet NaN so the bytes do not depend on NaN payload propagation.
+__device__ __forceinline__ uint32_t decode_bits(uint32_t code, float scale) {
+  const float y = (float)(int8_t)(code & 0xFFu) * scale;
+  return y != y ? 0x7FC00000u : as_uint(y);
+}
+
+// Largest value of `m` over the kLanes lanes (4, 8 or 16, aligned) that hold
+// one row, in every one of them: DPP lane swaps inside quads (xor 1, xor 2),
+// then the mirror inside each group of 8 (lane i with 7 - i pairs its two
+// quads) and inside each row of 16 (lane i with 15 - i pairs its two
+// groups of 8).  A row's lanes are active or idle together, so no read
+// crosses into a lane of another row.
+template <uint32_t kLanes>
+__device__ __forceinline__ float row_max(float m) {
+  static_assert(kLanes == 4 || kLanes == 8 || kLanes == 16, "lanes per row");
+  m = fmaxf(m, as_float(__builtin_amdgcn_update_dpp(0, (int)as_uint(m), 0xB1, 0xF, 0xF, false)));
+  m = fmaxf(m, as_float(__builtin_amdgcn_update_dpp(0, (int)as_uint(m), 0x4E, 0xF, 0xF, false)));
+  if (kLanes >= 8)
+    m = fmaxf(m, as_float(__builtin_amdgcn_update_dpp(0, (int)as_uint(m), 0x141, 0xF, 0xF, false)));
+  if (kLanes >= 16)
+    m = fmaxf(m, as_float(__builtin_amdgcn_update_dpp(0, (int)as_uint(m), 0x140, 0xF, 0xF, false)));
+  return m;
+}
+
+// INT8 codec of one group of recurrent-state rows (a KDA page under the
+// codec: conv part, then fp32 rows of kD values).  kLanes lanes hold a row:
+// lane `sub` holds the row's 16-byte vectors sub, sub + kLanes, ... (so the
+// kLanes lanes of a row read 16 * kLanes contiguous bytes per load) and the
+// matching 4-code words.  All of a lane's loads are issued before any use.
+// Store: the row's largest finite |x| (DPP reduction), then 4 codes per
+// vector and, from lane 0, the row's scale.  Retrieve: q * s back.
+// Quantisation (both sides of the parity tests take it in fp32, IEEE
+// division and round-half-even): s = max|x| / 127; q = rint(x / s) clamped
+// to [-127, 127]; 0 for non-finite x or s == 0 (Mooncake K3 blog, Compressed
+// Checkpoint Storage: per-channel INT8 of inactive recurrent states).
+template <uint32_t kD, bool kStore>
+__device__ __forceinline__ void codec_rows(const hkv::CopyArgs& a,
+                                           const HKV_CONST hkv::DevLayer* L, int32_t id,
+                                           uint8_t* obj_page, uint32_t group) {
+  constexpr uint32_t kLanes = hkv::codec_lanes_per_row(kD);
+  constexpr uint32_t kVecs = kD / (4 * kLanes);  // 16-byte vectors per lane
+  static_assert(kVecs >= 1 && kVecs * 4 * kLanes == kD, "a row splits into whole vectors");
+  constexpr uint32_t kRowsPerPass = kThreads / kLanes;
+  const uint32_t rows = L->codec_rows;
+  const uint32_t sub = threadIdx.x & (kLanes - 1);
+  const uint32_t r0 = group * a.codec_rows_per_item;
+  const uint32_t r_end = r0 + a.codec_rows_per_item < rows ? r0 + a.codec_rows_per_item : rows;
+  uint8_t* codes = obj_page + L->copy_bytes;
+  uint8_t* scales = codes + (uint64_t)rows * kD;
+  if (id < 0) {  // a null page: zeros in the object, nothing in the pool
+    if (kStore) {
+      zero_span(codes + (uint64_t)r0 * kD, (r_end - r0) * kD);
+      zero_span(scales + (uint64_t)r0 * 4, (r_end - r0) * 4);
+    }
+    return;
+  }
+  uint8_t* recurrent = a.pool + L->pool_offset + (uint64_t)id * L->stride + L->copy_bytes;
+  for (uint32_t r = r0 + threadIdx.x / kLanes; r < r_end; r += kRowsPerPass) {
+    HKV_GLOBAL v4u* xp = (HKV_GLOBAL v4u*)(recurrent + (uint64_t)r * kD * 4) + sub;
+    HKV_GLOBAL uint32_t* qp = (HKV_GLOBAL uint32_t*)(codes + (uint64_t)r * kD) + sub;
+    HKV_GLOBAL float* sp = (HKV_GLOBAL float*)scales + r;
+    if (kStore) {
+      v4u raw[kVecs];
+#pragma unroll
+      for (uint32_t v = 0; v < kVecs; ++v) raw[v] = load16(xp + v * kLanes);
+      float m = 0.0f;
+#pragma unroll
+      for (uint32_t v = 0; v < kVecs; ++v)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = as_float(raw[v][i]);
+          m = fmaxf(m, __builtin_isfinite(x) ? fabsf(x) : 0.0f);
+        }
+      m = row_max<kLanes>(m);
+      const float scale = m / 127.0f;
+#pragma unroll
+      for (uint32_t v = 0; v < kVecs; ++v) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = as_float(raw[v][i]);
+          const float t = fminf(fmaxf(rintf(x / scale), -127.0f), 127.0f);
+          const int q = (scale != 0.0f && __builtin_isfinite(x)) ? (int)t : 0;
+          packed |= ((uint32_t)q & 0xFFu) << (8 * i);
+        }
+        store4(qp + v * kLanes, packed);
+      }
+      if (sub == 0) store4((HKV_GLOBAL uint32_t*)sp, as_uint(scale));
+    } else {
+      uint32_t packed[kVecs];
+#pragma unroll
+      for (uint32_t v = 0; v < kVecs; ++v) packed[v] = load4(qp + v * kLanes);
+      const float scale = as_float(load4((const HKV_GLOBAL uint32_t*)sp));
+#pragma unroll
+      for (uint32_t v = 0; v < kVecs; ++v) {
+        v4u out;
+        out.x = decode_bits(packed[v], scale);
+        out.y = decode_bits(packed[v] >> 8, scale);
+        out.z = decode_bits(packed[v] >> 16, scale);
+        out.w = decode_bits(packed[v] >> 24, scale);
+        store16(xp + v * kLanes, out);
+      }
+    }
+  }
+}
+
+// The codec for the layer's head_dim (the planner admits 16..256, powers of two).
+template <bool kStore>
+__device__ __forceinline__ void codec_dispatch(const hkv::CopyArgs& a,
+                                               const HKV_CONST hkv::DevLayer* L, int32_t id,
+                                               uint8_t* obj_page, uint32_t group) {
+  switch (L->head_dim) {
+    case 16: codec_rows<16, kStore>(a, L, id, obj_page, group); break;
+    case 32: codec_rows<32, kStore>(a, L, id, obj_page, group); break;
+    case 64: codec_rows<64, kStore>(a, L, id, obj_page, group); break;
+    case 128: codec_rows<128, kStore>(a, L, id, obj_page, group); break;
+    case 256: codec_rows<256, kStore>(a, L, id, obj_page, group); break;
+    default: break;
+  }
+}
+
 template <bool kStore>
 __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a) {
   const HKV_CONST hkv::DevLayer* layers = (const HKV_CONST hkv::DevLayer*)a.layers;
@@ -133,18 +286,23 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a) {
     const uint64_t w = items[r];
     const uint32_t l = (uint32_t)(w & 0xFFFFu);
     const uint32_t j = (uint32_t)((w >> 16) & 0xFFFFu);
-    const uint32_t s = (uint32_t)(w >> 32);
+    const uint32_t s = (uint32_t)((w >> 32) & 0x7FFFFFFFu);
     const HKV_CONST hkv::DevLayer* L = layers + l;
-    const uint64_t page_bytes = L->page;
     const int32_t id = ids[((uint64_t)c * a.n_kv_groups + L->kv_group) * a.blocks_per_chunk + j];
     uint8_t* obj = reinterpret_cast<uint8_t*>(objs[(uint64_t)c * a.n_obj_groups + L->obj_group]);
+    uint8_t* obj_page = obj + L->obj_offset + (uint64_t)j * L->obj_page;
+    if (w >> 63) {  // a codec row group of a KDA page
+      codec_dispatch<kStore>(a, L, id, obj_page, s);
+      continue;
+    }
+    const uint64_t span = L->copy_bytes;  // the page, or the conv part under the codec
     const uint64_t off = (uint64_t)s * a.tile_bytes;
-    const uint64_t rest = page_bytes - off;
+    const uint64_t rest = span - off;
     const uint32_t bytes = (uint32_t)(rest < a.tile_bytes ? rest : a.tile_bytes);
-    uint8_t* obj_tile = obj + L->obj_offset + (uint64_t)j * page_bytes + off;
-    // Bytes of this page that hold data: all of it, none for a null id, and
+    uint8_t* obj_tile = obj_page + off;
+    // Bytes of this span that hold data: all of it, none for a null id, and
     // for an MLA page of a partial chunk the rows of its valid tokens.
-    uint64_t valid = id < 0 ? 0 : page_bytes;
+    uint64_t valid = id < 0 ? 0 : span;
     if (a.chunk_tokens && L->row_bytes && id >= 0) {
       int64_t rows = (int64_t)a.chunk_tokens[c] - (int64_t)j * (int64_t)a.block_tokens;
       rows = rows < 0 ? 0 : (rows > (int64_t)a.block_tokens ? (int64_t)a.block_tokens : rows);
@@ -165,11 +323,13 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a) {
 
 }  // namespace
 
-extern "C" __global__ __launch_bounds__(kThreads) void hkv_store_gather(hkv::CopyArgs a) {
+extern "C" __global__ __launch_bounds__(kThreads) HKV_OCCUPANCY
+void hkv_store_gather(hkv::CopyArgs a) {
   copy_items<true>(a);
 }
 
-extern "C" __global__ __launch_bounds__(kThreads) void hkv_retrieve_scatter(hkv::CopyArgs a) {
+extern "C" __global__ __launch_bounds__(kThreads) HKV_OCCUPANCY
+void hkv_retrieve_scatter(hkv::CopyArgs a) {
   copy_items<false>(a);
 }
 

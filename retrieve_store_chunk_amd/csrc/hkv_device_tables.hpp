@@ -7,24 +7,48 @@
 
 namespace hkv {
 
-// One layer's placement as the kernels see it (48 bytes).
+// One layer's placement as the kernels see it (80 bytes).
 struct DevLayer {
   uint64_t pool_offset;  // page of block 0
   uint64_t stride;       // bytes between block ids
   uint64_t obj_offset;   // page j = 0 inside the object
-  uint64_t page;         // real bytes of one page
+  uint64_t page;         // real bytes of one pool page
+  uint64_t obj_page;     // bytes one page takes in an object
+  uint64_t copy_bytes;   // bytes copied verbatim: the page, or the conv part under the codec
   uint32_t kv_group;
   uint32_t obj_group;
   uint32_t row_bytes;    // MLA: bytes per token row (a partial chunk keeps whole rows);
                          // KDA: 0 (a state page is whole or null)
-  uint32_t pad_;
+  uint32_t codec_rows;   // codec: rows of head_dim fp32 values (heads x head_dim); else 0
+  uint32_t head_dim;     // codec: values per row
+  uint32_t pad_[3];
 };
-static_assert(sizeof(DevLayer) == 48, "DevLayer layout");
+static_assert(sizeof(DevLayer) == 80, "DevLayer layout");
 
 // A work item of one chunk, packed in 64 bits: layer (16) | block j (16) |
-// tile index inside the page (32).
-inline constexpr uint64_t pack_item(uint32_t layer, uint32_t j, uint32_t tile) {
-  return (uint64_t)(layer & 0xFFFFu) | ((uint64_t)(j & 0xFFFFu) << 16) | ((uint64_t)tile << 32);
+// index (31) | kind (1).  Kind 0: verbatim tile `index` of the page's
+// copy_bytes; kind 1: codec row group `index`.
+inline constexpr uint64_t pack_item(uint32_t layer, uint32_t j, uint32_t index, uint32_t kind) {
+  return (uint64_t)(layer & 0xFFFFu) | ((uint64_t)(j & 0xFFFFu) << 16) |
+         ((uint64_t)(index & 0x7FFFFFFFu) << 32) | ((uint64_t)(kind & 1u) << 63);
+}
+
+#ifndef HKV_CODEC_VECS
+#define HKV_CODEC_VECS 2  // most 16-byte vectors a lane holds of a codec row (1..8)
+#endif
+static_assert(HKV_CODEC_VECS == 1 || HKV_CODEC_VECS == 2 || HKV_CODEC_VECS == 4 ||
+                  HKV_CODEC_VECS == 8,
+              "HKV_CODEC_VECS");
+
+// Lanes that hold one recurrent-state row of head_dim fp32 values in a codec
+// item: head_dim / (4 * HKV_CODEC_VECS), kept within 4..16 (a row's lanes
+// reduce with DPP inside one row of 16 lanes), so each lane holds
+// head_dim / (4 * lanes) 16-byte vectors.  A workgroup of `threads` lanes
+// takes threads / lanes rows a pass.
+inline constexpr uint32_t codec_lanes_per_row(uint32_t head_dim) {
+  return head_dim / (4 * HKV_CODEC_VECS) < 4    ? 4
+         : head_dim / (4 * HKV_CODEC_VECS) > 16 ? 16
+                                                : head_dim / (4 * HKV_CODEC_VECS);
 }
 
 // Kernel argument block (passed by value).
@@ -38,6 +62,7 @@ struct CopyArgs {
   uint64_t total_items;    // n_chunks * items_per_chunk
   uint64_t block_tokens;   // N
   uint64_t tile_bytes;
+  uint32_t codec_rows_per_item;  // rows quantized by one kind-1 item (whole passes)
   uint32_t items_per_chunk;
   uint32_t n_kv_groups;
   uint32_t blocks_per_chunk;

@@ -42,8 +42,9 @@ uint64_t object_fingerprint(const Plan& p) {
   fold((uint64_t)p.layers.size());
   for (int64_t v : p.shapes) fold((uint64_t)v);
   fold((uint64_t)p.n_obj_groups);
+  fold((uint64_t)p.kda_codec);
   for (const LayerPlacement& x : p.layers)
-    fold((uint64_t)x.is_mla | ((uint64_t)x.obj_group << 1) | (x.page << 8));
+    fold((uint64_t)x.is_mla | ((uint64_t)x.obj_group << 1) | (x.obj_page << 8));
   return f;
 }
 

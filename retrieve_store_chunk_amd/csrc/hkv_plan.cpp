@@ -15,6 +15,7 @@
 //    shared block stride): vLLM hybrid KV-cache blog, sections 3.1 and 3.2;
 //  - object groups: "Hybrid Attention Models", Object-group separation.
 #include "hkv_plan.hpp"
+#include "hkv_launch.hpp"
 
 #include <algorithm>
 #include <limits>
@@ -103,6 +104,20 @@ hkv_status make_plan(const hkv_layout_desc& d, Plan* p, std::string* err) {
   hkv_status st = model_sizes(m, &s, err);
   if (st != HKV_OK) return st;
   if (d.path != 0 && d.path != 1) return fail(err, HKV_E_ARG, "path must be 0 (A) or 1 (B)");
+  // The INT8 codec reads fp32 rows of head_dim values (a power of two from 16
+  // to 256, so one row maps onto 4..64 lanes) after a conv part of whole
+  // 16-byte units.
+  const int64_t conv_part = (int64_t)m.conv_dim * (m.conv_kernel - 1) * m.conv_bytes;
+  if (d.kda_codec != 0 && d.kda_codec != 1)
+    return fail(err, HKV_E_ARG, "kda_codec must be 0 or 1");
+  if (d.kda_codec == 1) {
+    const int32_t hd = m.kda_head_dim;
+    const bool pow2 = hd == 16 || hd == 32 || hd == 64 || hd == 128 || hd == 256;
+    if (m.kda_state_bytes != 4 || !pow2 || conv_part % 16 != 0)
+      return fail(err, HKV_E_ARG,
+                  "the INT8 codec needs an fp32 recurrent state, head_dim in {16..256} (a "
+                  "power of two) and a conv state of whole 16-byte units");
+  }
 
   // Block size N.
   int64_t n = 0;
@@ -142,6 +157,8 @@ hkv_status make_plan(const hkv_layout_desc& d, Plan* p, std::string* err) {
   const int64_t shapes[8] = {m.kda_heads, m.kda_head_dim, m.kda_state_bytes, m.conv_dim,
                              m.conv_kernel, m.conv_bytes, m.mla_width, m.mla_bytes};
   std::copy(shapes, shapes + 8, p->shapes);
+  p->kda_codec = d.kda_codec;
+  p->conv_part = (uint64_t)conv_part;
   p->chunk_tokens = k * n;
   p->path = d.path;
 
@@ -218,12 +235,17 @@ hkv_status make_plan(const hkv_layout_desc& d, Plan* p, std::string* err) {
   }
 
   // Object groups and the object byte layout (layer-major, then block j).
+  // Under the codec a KDA page takes conv part + rows codes + rows scales.
+  const uint64_t codec_rows = (uint64_t)m.kda_heads * (uint64_t)m.kda_head_dim;
+  const uint64_t codec_page = (uint64_t)conv_part + codec_rows * (uint64_t)m.kda_head_dim +
+                              codec_rows * 4;
   const bool split = d.separate_object_groups && s.n_kda > 0 && s.n_mla > 0;
   p->n_obj_groups = split ? 2 : 1;
   for (auto& x : p->layers) {
     x.obj_group = split ? x.is_mla : 0;
+    x.obj_page = (d.kda_codec == 1 && !x.is_mla) ? codec_page : x.page;
     x.obj_offset = p->obj_bytes[x.obj_group];
-    p->obj_bytes[x.obj_group] += (uint64_t)k * x.page;
+    p->obj_bytes[x.obj_group] += (uint64_t)k * x.obj_page;
   }
 
   // Copy decomposition.
@@ -232,22 +254,42 @@ hkv_status make_plan(const hkv_layout_desc& d, Plan* p, std::string* err) {
     return fail(err, HKV_E_ARG, "tile_bytes must be a multiple of 4096 up to 1 GiB");
   p->tile_bytes = tile;
   p->max_workgroups = d.max_workgroups;
+  // A codec item covers as many rows as one tile of fp32 input holds, in
+  // whole workgroup passes (at least one).
+  const uint64_t row_in = 4 * (uint64_t)m.kda_head_dim;
+  const uint64_t per_pass =
+      d.kda_codec == 1 ? kCopyThreads / codec_lanes_per_row((uint32_t)m.kda_head_dim) : 1;
+  p->codec_rows_per_item =
+      (uint32_t)(std::max<uint64_t>(1, tile / (row_in * per_pass)) * per_pass);
   p->dev_layers.clear();
   p->items.clear();
   for (int32_t l = 0; l < L; ++l) {
     const auto& x = p->layers[l];
+    const bool codec = d.kda_codec == 1 && !x.is_mla;
     DevLayer dl{};
     dl.pool_offset = x.pool_offset;
     dl.stride = x.stride;
     dl.obj_offset = x.obj_offset;
     dl.page = x.page;
+    dl.obj_page = x.obj_page;
+    dl.copy_bytes = codec ? (uint64_t)conv_part : x.page;
     dl.kv_group = (uint32_t)x.kv_group;
     dl.obj_group = (uint32_t)x.obj_group;
     dl.row_bytes = x.is_mla ? (uint32_t)s.tok_bytes : 0;
+    dl.codec_rows = codec ? (uint32_t)codec_rows : 0;
+    dl.head_dim = codec ? (uint32_t)m.kda_head_dim : 0;
     p->dev_layers.push_back(dl);
-    const uint64_t tiles = x.page ? (x.page + tile - 1) / tile : 0;
-    for (int64_t j = 0; j < k; ++j)
-      for (uint64_t t = 0; t < tiles; ++t) p->items.push_back(pack_item(l, (uint32_t)j, (uint32_t)t));
+    const uint64_t tiles = (dl.copy_bytes + tile - 1) / tile;
+    const uint64_t groups =
+        codec ? (codec_rows + p->codec_rows_per_item - 1) / p->codec_rows_per_item : 0;
+    if (tiles > 0x7FFFFFFFull || groups > 0x7FFFFFFFull)
+      return fail(err, HKV_E_ARG, "too many tiles per page");
+    for (int64_t j = 0; j < k; ++j) {
+      for (uint64_t t = 0; t < tiles; ++t)
+        p->items.push_back(pack_item(l, (uint32_t)j, (uint32_t)t, 0));
+      for (uint64_t g = 0; g < groups; ++g)
+        p->items.push_back(pack_item(l, (uint32_t)j, (uint32_t)g, 1));
+    }
   }
   if (p->items.size() > 0xFFFFFFFFull) return fail(err, HKV_E_ARG, "too many tiles per chunk");
   return HKV_OK;

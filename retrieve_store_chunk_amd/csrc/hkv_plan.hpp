@@ -22,6 +22,7 @@ struct LayerPlacement {
   uint64_t pool_offset = 0;    // block 0's page
   uint64_t stride = 0;         // between block ids
   uint64_t obj_offset = 0;     // block j = 0 inside the object
+  uint64_t obj_page = 0;       // bytes one page takes in an object
 };
 
 struct Plan {
@@ -41,10 +42,13 @@ struct Plan {
   // Per-rank model shapes: kda_heads, kda_head_dim, kda_state_bytes,
   // conv_dim, conv_kernel, conv_bytes, mla_width, mla_bytes.
   int64_t shapes[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int32_t kda_codec = 0;       // 1: INT8 codec of the KDA recurrent state in objects
+  uint64_t conv_part = 0;      // bytes of the conv state at the start of a KDA page
 
   // Copy decomposition: every (layer, block j, tile s) of one chunk is one
   // work item; the same list repeats for every chunk of a call.
   uint64_t tile_bytes = 0;
+  uint32_t codec_rows_per_item = 0;
   uint32_t max_workgroups = 0;
   std::vector<DevLayer> dev_layers;
   std::vector<uint64_t> items;  // packed WorkItem per item of one chunk

@@ -61,7 +61,7 @@ def same_plan(desc):
     return got
 
 
-@pytest.mark.parametrize("name", workloads.CONFIG_NAMES)
+@pytest.mark.parametrize("name", workloads.CONFIG_NAMES + workloads.EXTRA_CONFIG_NAMES)
 def test_planner_matches_oracle_on_workloads(name):
     same_plan(workloads.make_config(name).desc)
     same_plan(workloads.make_small_config(name).desc)
@@ -99,6 +99,24 @@ def test_planner_matches_oracle_on_random_layouts(params, block_size, strict, bu
     assert st_got == st_ref
     if st_ref == 0:
         same_plan(d)
+
+
+@settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(st.lists(st.integers(0, 1), min_size=1, max_size=6), st.integers(1, 3),
+       st.sampled_from([8, 16, 32, 48, 64, 256]), st.sampled_from([0, 4, 5, 8, 104]),
+       st.sampled_from([2, 4]), st.sampled_from([0, 1, 2]), st.integers(0, 1), st.integers(0, 1),
+       st.sampled_from([0, 4096, 8192, 1 << 20]))
+def test_codec_layouts_match_oracle(is_mla, heads, head_dim, conv, state_bytes, codec, path, sep,
+                                    tile):
+    """The INT8 codec's shape rules and object layout: same status and the
+    same placement (object page bytes included) as the oracle."""
+    d = workloads._desc(is_mla, heads, head_dim, conv, 2, path, 1 << 30, separate=sep,
+                        state_bytes=state_bytes, mla_width=64, kda_codec=codec)
+    st_ref = status_oracle(d)
+    assert hkv.status_of(hkv.hkv_layout_init, dict(d, tile_bytes=tile)) == st_ref
+    if st_ref == 0:
+        same_plan(dict(d, tile_bytes=tile))
+        assert hkv.Layout(d).fingerprint() == oracle.Layout(d).fingerprint()
 
 
 def test_layout_errors_match_oracle():

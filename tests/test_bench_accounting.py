@@ -1,0 +1,50 @@
+"""The benchmark's byte accounting (no GPU): the payload and HBM bytes of a
+call, counted page by page from the oracle's placement, with null pages,
+partial chunks and INT8 KDA pages."""
+import copy
+
+import numpy as np
+import pytest
+
+import bench
+import oracle
+import retrieve_store_chunk_amd as hkv
+import workloads as W
+
+
+def brute(ref, w):
+    N, k = ref.summary["block_size"], ref.k
+    data = live = 0
+    for ci in range(len(w.chunks)):
+        t = N * k if w.chunk_tokens is None else int(w.chunk_tokens[ci])
+        for L in ref.layers:
+            for j in range(k):
+                if int(w.ids[ci, L["kv_group"], j]) == W.NULL_BLOCK:
+                    continue
+                if L["is_mla"]:
+                    rows = min(N, max(0, t - j * N))
+                    data += rows * (L["page_bytes"] // N)
+                    live += rows * (L["page_bytes"] // N)
+                else:
+                    data += L["page_bytes"]
+                    live += L["obj_page_bytes"]
+    return data, len(w.chunks) * (ref.summary["obj_bytes0"] + ref.summary["obj_bytes1"]), live
+
+
+@pytest.mark.parametrize("name,codec", [("tiny", 0), ("tiny", 1), ("k3_tp8_holes", 0),
+                                        ("k3_tp8_holes", 1), ("kl_tp1_tails", 1),
+                                        ("kl_tp1_int8", 1)])
+def test_wave_bytes_match_page_by_page_count(name, codec):
+    cfg = copy.deepcopy(W.make_small_config(name))
+    cfg.desc = dict(cfg.desc, kda_codec=codec)
+    ref, lay = oracle.Layout(cfg.desc), hkv.Layout(cfg.desc)
+    s = ref.summary
+    kda = tuple(g for g in range(ref.G)
+                if not any(L["is_mla"] for L in ref.layers if L["kv_group"] == g))
+    waves = W.plan_waves(cfg, s["num_blocks"], ref.G, ref.k, kda_groups=kda,
+                         block_tokens=s["block_size"], chunk_tokens=s["chunk_tokens"])
+    for w in waves:
+        got = bench.wave_bytes(lay, w)
+        assert got == brute(ref, w)
+        if not codec:
+            assert got[0] == got[2]

@@ -240,3 +240,4 @@ def test_decode_of_objects_the_encoder_did_not_write():
     assert np.array_equal(y[3].view(np.float32), codes[3].astype(np.float32) * np.float32(-0.5))
     want4 = (codes[4].astype(np.float64) * 3 * 2.0 ** -149).astype(np.float32)
     assert np.array_equal(y[4].view(np.float32), want4)
+

@@ -7,7 +7,9 @@ the pool and object bytes are the counter-based SplitMix64 stream, so the
 expected bytes of any page or object range are computed on the host from the
 seed and the oracle's placement of that page.  Also checked on samples:
 store leaves the pool unchanged; retrieve leaves padding, group slack and
-untargeted blocks unchanged.
+untargeted blocks unchanged.  Under the INT8 codec the expected object page
+is the oracle's encoding of the expected pool page, and a retrieved page the
+oracle's decoding of the expected object page.
 """
 import numpy as np
 import pytest
@@ -59,7 +61,7 @@ def test_full_size_sampled(name):
     g.fill_objects(W.derive_seed(cfg.seed, 77))
     g.stream.synchronize()
     retrieved_since_fill = set()
-    stats = {"tiles": 0, "bytes": 0}
+    stats = {"tiles": 0, "bytes": 0, "codec": 0}
 
     def page_at(l, block):
         L = Ls[l]
@@ -88,31 +90,41 @@ def test_full_size_sampled(name):
             rc = w.chunks[ci]
             L = Ls[l]
             o, grp = L["obj_group"], L["kv_group"]
-            obj_lo = L["obj_offset"] + j * L["page_bytes"]
+            obj_n = L["obj_page_bytes"]
+            obj_lo = L["obj_offset"] + j * obj_n
+            codec = obj_n != L["page_bytes"]   # a KDA page in INT8 form
             bid = int(w.ids[ci, grp, j])
             if w.op == "store":
                 if bid == W.NULL_BLOCK:   # a null page is zeros in the object
-                    got = _d2h(g.object_view(rc, o), obj_lo, L["page_bytes"])
+                    got = _d2h(g.object_view(rc, o), obj_lo, obj_n)
                     assert not got.any(), f"store wave {i} chunk {rc} layer {l} j {j}: null"
                     continue
                 off, nbytes = page_at(l, bid)
                 v = valid(l, j, w, ci)
-                want = W.fill_bytes(g.pool_seed_of[rc], off, nbytes)
-                got = _d2h(g.object_view(rc, o), obj_lo, nbytes)
-                assert np.array_equal(got[:v], want[:v]), \
-                    f"store wave {i} chunk {rc} layer {l} j {j}"
-                assert not got[v:].any()
+                src = W.fill_bytes(g.pool_seed_of[rc], off, nbytes)
+                want = ref.codec_page(src, True, l) if codec else src
+                got = _d2h(g.object_view(rc, o), obj_lo, obj_n)
+                if codec:
+                    assert np.array_equal(got, want), f"store wave {i} chunk {rc} layer {l} j {j}"
+                else:
+                    assert np.array_equal(got[:v], want[:v]), \
+                        f"store wave {i} chunk {rc} layer {l} j {j}"
+                    assert not got[v:].any()
                 # the source page is unchanged
-                assert np.array_equal(_d2h(g.pool, off, nbytes), want)
+                assert np.array_equal(_d2h(g.pool, off, nbytes), src)
             else:
                 if bid == W.NULL_BLOCK:
                     continue
                 v = valid(l, j, w, ci)
                 if w.prefilled_objects:
-                    want = W.fill_bytes(W.derive_seed(W.object_seed(cfg, *rc), o), obj_lo, v)
+                    obj_seed = W.derive_seed(W.object_seed(cfg, *rc), o)
+                    want = (ref.codec_page(W.fill_bytes(obj_seed, obj_lo, obj_n), False, l)
+                            if codec else W.fill_bytes(obj_seed, obj_lo, v))
                 else:
                     soff, _ = page_at(l, g.store_ids[rc][grp, j])
                     want = W.fill_bytes(g.pool_seed_of[rc], soff, v)
+                    if codec:
+                        want = ref.codec_page(ref.codec_page(want, True, l), False, l)
                 off, nbytes = page_at(l, bid)
                 got = _d2h(g.pool, off, v)
                 assert np.array_equal(got, want), f"retrieve wave {i} chunk {rc} layer {l} j {j}"
@@ -128,6 +140,7 @@ def test_full_size_sampled(name):
                                           W.fill_bytes(fill_seed, pad_lo, pad_n))
             stats["tiles"] += 1
             stats["bytes"] += L["page_bytes"]
+            stats["codec"] += int(codec)
         if path == 1 and w.op == "retrieve":
             # group slack [group total, block stride) of targeted blocks
             totals = {}
@@ -152,6 +165,6 @@ def test_full_size_sampled(name):
     g.run_all(on_wave=on_wave)
     g.stream.synchronize()
     print(f"[fullsize] {name}: {len(g.waves)} waves, {stats['tiles']} sampled pages "
-          f"({stats['bytes'] / 1e6:.1f} MB) match", flush=True)
+          f"({stats['bytes'] / 1e6:.1f} MB, {stats['codec']} in INT8 form) match", flush=True)
     del g
     torch.cuda.empty_cache()

@@ -110,11 +110,11 @@ def test_pathological_bit_patterns():
 
 def mini_config(name, is_mla, path, sep=1, grouping=None, chunk_min=1, conv_dim=4,
                 mla_width=8, mla_bytes=1, heads=1, head_dim=4, blocks=12, requests=(2, 1, 3),
-                retrieve_first=None):
+                retrieve_first=None, codec=0):
     """A small layout with a given shape; the pool holds `blocks` blocks."""
     desc = W._desc(is_mla, heads, head_dim, conv_dim, mla_bytes, path, 1 << 30,
                    chunk_min=chunk_min, kv_group_of_layer=grouping, separate=sep,
-                   mla_width=mla_width)
+                   mla_width=mla_width, kda_codec=codec)
     probe = oracle.Layout(desc).summary
     per_block = probe["pool_bytes_used"] // probe["num_blocks"]
     desc["pool_bytes"] = blocks * per_block + 5
@@ -284,3 +284,113 @@ def test_objects_move_between_pool_layouts_with_equal_fingerprints():
     for n, rc in enumerate(store.chunks):
         for o in range(ref_a.O):
             assert np.array_equal(ga.host_object(rc, o), objs_b[n][o])
+
+
+# ------------------------------------------------------------ INT8 codec
+def with_codec(cfg):
+    import copy
+    cfg = copy.deepcopy(cfg)
+    cfg.desc = dict(cfg.desc, kda_codec=1)
+    cfg.name += "_int8"
+    return cfg
+
+
+@pytest.mark.parametrize("name", ["kl_tp1_int8", "tiny", "kl_tp2", "k3_tp8", "long_ctx",
+                                  "k3_tp8_holes", "kl_tp1_tails"])
+def test_codec_workload_parity_small(name):
+    """Workload shapes under the INT8 codec.  The pool and objects are random
+    bytes, so the fp32 states span every bit pattern (NaNs with payloads,
+    infinities, denormals, every exponent) and the long-context retrieve
+    decodes objects no encoder wrote."""
+    cfg = W.make_small_config(name)
+    run_parity(cfg if cfg.desc.get("kda_codec") else with_codec(cfg))
+
+
+CODEC_EDGE = [
+    # d = 16 (4 lanes a row), conv part of 3 x 16 bytes
+    mini_config("codec_d16", [0, 0, 1], 0, heads=1, head_dim=16, conv_dim=8, codec=1),
+    # no conv part, odd MLA pages (byte path beside the codec)
+    mini_config("codec_d32_noconv", [0, 1, 0, 1], 1, heads=2, head_dim=32, conv_dim=0,
+                mla_width=9, codec=1),
+    # d = 64, two blocks per chunk, conv part of several tiles
+    mini_config("codec_d64_k2", [0, 1, 0], 0, heads=3, head_dim=64, conv_dim=104,
+                mla_width=1024, mla_bytes=2, chunk_min=40, blocks=30, codec=1),
+    # d = 256 (a whole wavefront per row), one object for every layer
+    mini_config("codec_d256_merged", [0, 0, 1], 1, sep=0, heads=1, head_dim=256, conv_dim=8,
+                mla_width=512, mla_bytes=2, blocks=16, codec=1),
+    mini_config("codec_only_kda", [0, 0, 0], 1, heads=2, head_dim=16, conv_dim=8, blocks=9,
+                codec=1),
+]
+
+
+def codec_rows(rng, n, d):
+    """n rows of d fp32 values from eight recipes: Gaussian at random scales,
+    exact ties (largest |x| = 127 * 2^e, the rest (m + 1/2) * 2^e), exact
+    power-of-two lattices, denormals, zero rows, NaN / inf sprinkled into a
+    row, rows with nothing finite, and values near the fp32 maximum."""
+    kind = rng.integers(0, 8, n)
+    e = np.exp2(rng.integers(-30, 30, (n, 1))).astype(np.float32)
+    x = (rng.standard_normal((n, d)) * 10.0 ** rng.uniform(-3, 3, (n, 1))).astype(np.float32)
+    ties = ((rng.integers(-127, 127, (n, d)) + 0.5) * e).astype(np.float32)
+    ties[:, 0] = 127 * e[:, 0] * np.where(rng.random(n) < 0.5, -1, 1)
+    lattice = (rng.integers(-127, 128, (n, d)) * e).astype(np.float32)
+    denorm = (rng.standard_normal((n, d)) * 1e-39).astype(np.float32)
+    zero = np.where(rng.random((n, d)) < 0.5, 0.0, -0.0).astype(np.float32)
+    sprinkled = x.copy()
+    hit = rng.random((n, d)) < 0.1
+    sprinkled[hit] = rng.choice(np.array([np.nan, np.inf, -np.inf], np.float32), hit.sum())
+    nothing = rng.choice(np.array([np.nan, np.inf, -np.inf], np.float32), (n, d))
+    huge = (rng.uniform(-1, 1, (n, d)) * np.finfo(np.float32).max).astype(np.float32)
+    out = np.choose(kind[:, None], [x, ties, lattice, denorm, zero, sprinkled, nothing, huge])
+    return out.astype(np.float32)
+
+
+def codec_fill(desc):
+    """A pool fill: random bytes, with every KDA page's recurrent rows (in
+    every block) drawn from codec_rows."""
+    ref = oracle.Layout(desc)
+    d = desc["kda_head_dim"]
+    rows = desc["kda_heads"] * d
+    conv = desc["conv_dim"] * (desc["conv_kernel"] - 1) * desc["conv_bytes"]
+
+    def fill(nbytes, seed):
+        out = W.fill_bytes(seed, 0, nbytes)
+        rng = np.random.default_rng(seed % (1 << 32))
+        for L in ref.layers:
+            if L["is_mla"]:
+                continue
+            for b in range(ref.summary["num_blocks"]):
+                lo = L["pool_offset"] + b * L["stride"] + conv
+                out[lo: lo + rows * d * 4] = codec_rows(rng, rows, d).view(np.uint8).ravel()
+        return out
+    return fill
+
+
+@pytest.mark.parametrize("cfg", [with_codec(W.make_config("tiny"))] + CODEC_EDGE,
+                         ids=lambda c: c.name)
+def test_codec_value_recipes(cfg):
+    """Rows built to hit every branch of the quantiser: bit-exact codes,
+    scales and decoded states against the oracle."""
+    run_parity(cfg, pool_fill=codec_fill(cfg.desc))
+
+
+@pytest.mark.parametrize("cfg", CODEC_EDGE, ids=lambda c: c.name)
+@pytest.mark.parametrize("tile,max_wg", [(0, 0), (8192, 7), (1 << 20, 1)])
+def test_codec_edge_layouts_and_tuning(cfg, tile, max_wg):
+    """Rows per codec item follow the tile size; results do not."""
+    run_parity(cfg, tile_bytes=tile, max_workgroups=max_wg)
+
+
+@pytest.mark.parametrize("cfg", [holes_and_tails(CODEC_EDGE[0], 2, 5),
+                                 holes_and_tails(CODEC_EDGE[2], 3, 33),
+                                 holes_and_tails(CODEC_EDGE[3], 1, 100)],
+                         ids=lambda c: c.name)
+def test_codec_with_holes_and_tails(cfg):
+    """Null KDA pages (codes and scales zeroed on store, nothing written on
+    retrieve) beside partial MLA chunks."""
+    run_parity(cfg, pool_fill=codec_fill(cfg.desc))
+    run_parity(cfg, tile_bytes=4096, max_workgroups=5)
+
+
+def test_codec_host_objects():
+    run_parity(W.make_small_config("kl_tp1_int8"), objects="host")

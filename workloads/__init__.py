@@ -161,14 +161,14 @@ K3_93 = kkkm_pattern(92, tail_mla=1)
 
 def _desc(is_mla, heads, head_dim, conv_dim, mla_bytes, path, pool_bytes, block_size=0,
           chunk_min=1, kv_group_of_layer=None, separate=1, state_bytes=4, conv_kernel=4,
-          conv_bytes=2, mla_width=576, strict=0, max_batched=0) -> dict:
+          conv_bytes=2, mla_width=576, strict=0, max_batched=0, kda_codec=0) -> dict:
     return dict(is_mla=list(is_mla), kda_heads=heads, kda_head_dim=head_dim,
                 kda_state_bytes=state_bytes, conv_dim=conv_dim, conv_kernel=conv_kernel,
                 conv_bytes=conv_bytes, mla_width=mla_width, mla_bytes=mla_bytes,
                 block_size=block_size, chunk_min_tokens=chunk_min, strict_chunk_multiple=strict,
                 path=path, separate_object_groups=separate,
                 kv_group_of_layer=kv_group_of_layer, pool_bytes=pool_bytes,
-                max_num_batched_tokens=max_batched)
+                max_num_batched_tokens=max_batched, kda_codec=kda_codec)
 
 
 @dataclass
@@ -292,12 +292,23 @@ def make_config(name: str) -> Config:
                        Phase("retrieve", _all_chunks(req), tail_tokens=tails)], seed,
                       notes="each request stores its whole first chunk and a partial second "
                             "chunk (160 MLA rows, no KDA snapshot: its block is not complete)")
+    if name == "kl_tp1_int8":
+        seed = 0x48B0009
+        req = [8] * 128
+        desc = _desc(KIMI_LINEAR_27, 32, 128, 12288, 2, 1, 64 * GIB, kda_codec=1)
+        return Config(name, "Kimi-Linear full state (TP=1), path B, KDA recurrent state "
+                      "stored as per-row INT8", desc, req,
+                      [Phase("store", _all_chunks(req)),
+                       Phase("retrieve", _all_chunks(req, first=4))], seed,
+                      notes="the Kimi-Linear TP=1 workload with the INT8 codec of KDA "
+                            "checkpoints: 3.5x smaller KDA objects, quantised on store and "
+                            "dequantised on retrieve in the same pass")
     raise KeyError(name)
 
 
 CONFIG_NAMES = ("tiny", "kl_tp2", "kl_tp1", "k3_tp8", "long_ctx")
 # Further workloads beyond the five above.
-EXTRA_CONFIG_NAMES = ("kl_tp1_host", "k3_tp8_holes", "kl_tp1_tails")
+EXTRA_CONFIG_NAMES = ("kl_tp1_host", "k3_tp8_holes", "kl_tp1_tails", "kl_tp1_int8")
 
 
 def make_small_config(name: str) -> Config:
@@ -322,6 +333,11 @@ def make_small_config(name: str) -> Config:
         cfg.requests = [2] * 7
         cfg.phases = [Phase("store", _all_chunks(cfg.requests)),
                       Phase("retrieve", _all_chunks(cfg.requests))]
+    elif name == "kl_tp1_int8":
+        cfg.desc["pool_bytes"] = 1 * GIB
+        cfg.requests = [4] * 5
+        cfg.phases = [Phase("store", _all_chunks(cfg.requests)),
+                      Phase("retrieve", _all_chunks(cfg.requests, first=2))]
     elif name == "kl_tp1_host":
         cfg.desc["pool_bytes"] = 1 * GIB
         cfg.requests = [4] * 3
