@@ -83,12 +83,27 @@ def wave_bytes(layout, w) -> tuple:
     return data, n * info["chunk_payload_bytes"], live
 
 
-def cpu_baseline(cfg, min_seconds: float = 10.0, max_seconds: float = 30.0) -> dict:
-    """The oracle (plain C, one thread, one memcpy per page, or its INT8 codec
-    loop for KDA pages when the layout has one) on a bounded
-    sample of the same workload: the same layout shapes in a smaller pool,
-    64 chunks stored and their first halves retrieved into fresh ids,
-    repeated until at least min_seconds of CPU time."""
+def cpu_threads() -> int:
+    """Host threads for the threaded oracle leg: the CPUs this process may
+    use, at most 16 (one GPU's share of a host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(cfg, threads: int = 1, min_seconds: float = 10.0,
+                 max_seconds: float = 30.0) -> dict:
+    """The oracle (plain C, one memcpy per page, or its INT8 codec loop for
+    KDA pages when the layout has one) on a bounded sample of the same
+    workload: the same layout shapes in a smaller pool, 64 chunks stored and
+    their first halves retrieved into fresh ids, repeated until at least
+    min_seconds of wall time.  With threads > 1 the unchanged oracle runs on
+    that many host threads, each storing (then retrieving) its own slice of
+    the chunks; ctypes releases the GIL inside the calls."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import oracle
     import workloads as W
@@ -111,19 +126,35 @@ def cpu_baseline(cfg, min_seconds: float = 10.0, max_seconds: float = 30.0) -> d
     ret_ids = perm2[: n_ret * ids_per_chunk].reshape(n_ret, lay.G, lay.k)
     # pool page bytes per chunk (the objects' size, unless KDA pages are INT8)
     payload = (n_store + n_ret) * lay.k * sum(L["page_bytes"] for L in lay.layers)
-    passes, t_cpu = 0, 0.0
-    while t_cpu < min_seconds and (passes == 0 or t_cpu + t_cpu / passes < max_seconds):
-        c0 = time.perf_counter()
-        lay.store(pool, store_ids, objs)
-        lay.retrieve(pool, ret_ids, objs[:n_ret])
-        t_cpu += time.perf_counter() - c0
-        passes += 1
-    gbs = passes * payload / t_cpu / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    threads = max(1, min(threads, n_ret))
+    st_parts = np.array_split(np.arange(n_store), threads)
+    rt_parts = np.array_split(np.arange(n_ret), threads)
+
+    def store_part(ix):
+        lay.store(pool, store_ids[ix], [objs[i] for i in ix])
+
+    def retrieve_part(ix):
+        lay.retrieve(pool, ret_ids[ix], [objs[i] for i in ix])
+
+    passes, t_wall = 0, 0.0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while t_wall < min_seconds and (passes == 0 or t_wall + t_wall / passes < max_seconds):
+            c0 = time.perf_counter()
+            if threads == 1:
+                lay.store(pool, store_ids, objs)
+                lay.retrieve(pool, ret_ids, objs[:n_ret])
+            else:
+                list(ex.map(store_part, st_parts))
+                list(ex.map(retrieve_part, rt_parts))
+            t_wall += time.perf_counter() - c0
+            passes += 1
+    gbs = passes * payload / t_wall / 1e9
+    how = "single-threaded" if threads == 1 else f"{threads} host threads, chunks split evenly"
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{passes} passes of: store {n_store} chunks + retrieve {n_ret} chunks "
                       f"(same page shapes, pool of {s['num_blocks']} blocks); "
-                      f"{passes * payload / 1e9:.1f} GB moved in {t_cpu:.1f} s wall, "
-                      "single-threaded plain C memcpy"
+                      f"{passes * payload / 1e9:.1f} GB moved in {t_wall:.1f} s wall, "
+                      f"{how}, plain C memcpy"
                       + (" + per-row INT8 codec of KDA pages" if s["kda_codec"] else "")}
 
 
@@ -403,6 +434,10 @@ def main() -> int:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(cfg)
         log(f"cpu baseline: {out['cpu_baseline']['value']} GB/s")
+        nt = cpu_threads()
+        if nt > 1:
+            out["cpu_baseline_threads"] = cpu_baseline(cfg, threads=nt)
+            log(f"cpu baseline, {nt} threads: {out['cpu_baseline_threads']['value']} GB/s")
     print(json.dumps(out), flush=True)
     return 0
 
