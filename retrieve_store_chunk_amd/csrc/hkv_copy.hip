@@ -12,13 +12,16 @@
 //     contiguous, with nontemporal hints (the pools are far larger than the
 //     caches and nothing is reused);
 //   - workgroups go round-robin over the 8 XCDs, so the item index is remapped
-//     to give each XCD one contiguous range of tiles: at any moment the
-//     workgroups of an XCD sweep a narrow window of a few pages instead of
-//     striding across the whole batch;
-//   - tiles are small (4 KiB by default) so that a window stays narrow: on
-//     MI355X this measured best for both directions (about 6.9 TB/s of HBM
-//     traffic for the gather and 6.3 TB/s for the scatter at the Kimi-Linear
-//     TP=1 shapes, against 6.1 and 5.2 TB/s with 256 KiB tiles and no remap);
+//     so that the workgroups of an XCD sweep a narrow window of a few pages
+//     instead of striding across the whole batch.  The gather gives each XCD
+//     one contiguous range of items; the scatter lets the XCDs take turns on
+//     runs of 8192 items (32 MiB), so that they work on neighbouring pages;
+//   - tiles are small (4 KiB by default) so that a window stays narrow; the
+//     gather issues two 16-byte loads per lane before its stores, the
+//     scatter one.  On MI355X these measured best per direction (about
+//     6.9 TB/s of HBM traffic for the gather and 6.4 TB/s for the scatter at
+//     the Kimi-Linear TP=1 shapes, against 6.1 and 5.2 TB/s with 256 KiB
+//     tiles and no remap);
 //   - only real page bytes are touched, so KDA padding (path A) and group
 //     slack (path B) are never read or written.
 // A page is opaque bytes ("Kimi-Linear" recipe: the KDA state is an opaque
@@ -35,8 +38,11 @@
 namespace {
 
 // Build-time choices (defaults are the tuned ones).
-#ifndef HKV_UNROLL
-#define HKV_UNROLL 1      // 16-byte loads per lane issued before their stores
+#ifndef HKV_STORE_UNROLL
+#define HKV_STORE_UNROLL 2     // gather: 16-byte loads per lane issued before their stores
+#endif
+#ifndef HKV_RETRIEVE_UNROLL
+#define HKV_RETRIEVE_UNROLL 1  // scatter: the same
 #endif
 #ifndef HKV_NT_LOAD
 #define HKV_NT_LOAD 1     // nontemporal loads
@@ -46,6 +52,12 @@ namespace {
 #endif
 #ifndef HKV_XCD_REMAP
 #define HKV_XCD_REMAP 1   // give each XCD a contiguous range of work items
+#endif
+#ifndef HKV_STORE_XCD_RUN
+#define HKV_STORE_XCD_RUN 0        // gather: >0 = XCDs take turns on runs of this many items
+#endif
+#ifndef HKV_RETRIEVE_XCD_RUN
+#define HKV_RETRIEVE_XCD_RUN 8192  // scatter: the same
 #endif
 #ifndef HKV_CODEC_NT
 #define HKV_CODEC_NT 1    // nontemporal code / scale accesses in the codec
@@ -60,7 +72,6 @@ namespace {
 #endif
 
 constexpr uint32_t kThreads = hkv::kCopyThreads;
-constexpr uint32_t kUnroll = HKV_UNROLL;
 constexpr uint32_t kXcds = 8;  // MI355X: workgroups go round-robin over 8 XCDs
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
@@ -85,6 +96,7 @@ __device__ __forceinline__ void store16(HKV_GLOBAL v4u* p, v4u v) {
 // workgroup.  Spans whose pointers and length are 16-byte multiples take the
 // vector path; anything else (pages whose size is not a 16-byte multiple)
 // falls back to byte copies.
+template <uint32_t kUnroll>
 __device__ __forceinline__ void copy_span(uint8_t* dst, const uint8_t* src, uint32_t bytes) {
   const uint32_t t = threadIdx.x;
   if (((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src) | bytes) & 15u) ==
@@ -264,7 +276,7 @@ __device__ __forceinline__ void codec_dispatch(const hkv::CopyArgs& a,
   }
 }
 
-template <bool kStore>
+template <bool kStore, uint32_t kUnroll, uint32_t kRun>
 __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a) {
   const HKV_CONST hkv::DevLayer* layers = (const HKV_CONST hkv::DevLayer*)a.layers;
   const HKV_CONST uint64_t* items = (const HKV_CONST uint64_t*)a.items;
@@ -272,11 +284,29 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a) {
   const HKV_CONST uint64_t* objs = (const HKV_CONST uint64_t*)a.objs;
   const uint32_t total = (uint32_t)a.total_items;
 #if HKV_XCD_REMAP
-  // Workgroup b runs on XCD b % 8; give XCD x the contiguous item range
-  // [x*q + min(x, r), ...) of this round so one XCD works through whole pages.
-  const uint32_t q = gridDim.x / kXcds, r = gridDim.x % kXcds;
+  // Workgroup b runs on XCD b % 8.
   const uint32_t x = blockIdx.x % kXcds;
-  const uint32_t first = x * q + (x < r ? x : r) + blockIdx.x / kXcds;
+  uint32_t first;
+  if (kRun == 0) {
+    // XCD x takes the contiguous item range [x*q + min(x, r), ...) of this
+    // round, so one XCD works through whole pages.
+    const uint32_t q = gridDim.x / kXcds, r = gridDim.x % kXcds;
+    first = x * q + (x < r ? x : r) + blockIdx.x / kXcds;
+  } else {
+    // In each span of 8 runs of kRun items XCD x takes run x, in order, so
+    // the XCDs work side by side on neighbouring runs; the last partial span
+    // is split into one contiguous range per XCD.
+    const uint32_t run = kRun ? kRun : 1;
+    const uint32_t full = gridDim.x / (kXcds * run) * (kXcds * run);
+    if (blockIdx.x < full) {
+      const uint32_t j = blockIdx.x / kXcds;
+      first = (j / run) * (kXcds * run) + x * run + (j % run);
+    } else {
+      const uint32_t t = blockIdx.x - full, n = gridDim.x - full;
+      const uint32_t q = n / kXcds, r = n % kXcds;
+      first = full + x * q + (x < r ? x : r) + t / kXcds;
+    }
+  }
 #else
   const uint32_t first = blockIdx.x;
 #endif
@@ -313,9 +343,9 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a) {
     if (live) {
       uint8_t* page = a.pool + L->pool_offset + (uint64_t)id * L->stride + off;
       if (kStore)
-        copy_span(obj_tile, page, live);
+        copy_span<kUnroll>(obj_tile, page, live);
       else
-        copy_span(page, obj_tile, live);
+        copy_span<kUnroll>(page, obj_tile, live);
     }
     if (kStore && live < bytes) zero_span(obj_tile + live, bytes - live);
   }
@@ -325,12 +355,12 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a) {
 
 extern "C" __global__ __launch_bounds__(kThreads) HKV_OCCUPANCY
 void hkv_store_gather(hkv::CopyArgs a) {
-  copy_items<true>(a);
+  copy_items<true, HKV_STORE_UNROLL, HKV_STORE_XCD_RUN>(a);
 }
 
 extern "C" __global__ __launch_bounds__(kThreads) HKV_OCCUPANCY
 void hkv_retrieve_scatter(hkv::CopyArgs a) {
-  copy_items<false>(a);
+  copy_items<false, HKV_RETRIEVE_UNROLL, HKV_RETRIEVE_XCD_RUN>(a);
 }
 
 namespace hkv {
