@@ -229,8 +229,10 @@ hkv_status hkv_workspace_size(const hkv_layout* layout, int32_t max_chunks, size
 
 /* Store (gather): for every chunk c, layer l and block j < k, copies the
  * page_bytes(l) bytes at pool + pool_offset(l) + block_ids[c][g(l)][j] x
- * stride(l) to objects[c][o(l)] + obj_offset(l) + j x page_bytes(l).
- * Padding and group slack are never read.  The pool is not modified.
+ * stride(l) to objects[c][o(l)] + obj_offset(l) + j x obj_page_bytes(l)
+ * (obj_page_bytes = page_bytes, except KDA pages under kda_codec = 1, which
+ * are written in their INT8 form).  Padding and group slack are never read.
+ * The pool is not modified.
  * pool: DEVICE, 16-byte aligned, pool_bytes_used long.  workspace: DEVICE,
  * 16-byte aligned, ws_bytes >= hkv_workspace_size(n_chunks); it is
  * overwritten and must not be used by another call until the stream passes
@@ -239,7 +241,8 @@ hkv_status hkv_workspace_size(const hkv_layout* layout, int32_t max_chunks, size
  * HKV_NULL_BLOCK and hkv_chunk_batch.chunk_tokens.
  * Errors: HKV_E_ARG (also a chunk_tokens entry outside [0, C]), HKV_E_RANGE
  * (an id neither HKV_NULL_BLOCK nor in [0, num_blocks)), HKV_E_ALIAS (objects
- * overlap each other or the pool), HKV_E_ALIGN, HKV_E_WORKSPACE, HKV_E_HIP. */
+ * overlap each other, the pool or the workspace), HKV_E_ALIGN,
+ * HKV_E_WORKSPACE, HKV_E_HIP (a HIP call failed; hkv_last_error names it). */
 hkv_status hkv_store_chunks(const hkv_layout* layout, const void* pool,
                             const hkv_chunk_batch* batch, void* workspace, size_t ws_bytes,
                             void* stream);

@@ -117,7 +117,12 @@ hkv_status upload(void* dst, size_t bytes, hipStream_t stream, Fill fill) {
   e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_error(e, "hipMemcpyAsync (tables)");
   e = hipEventRecord(s.done, stream);
-  if (e != hipSuccess) return hip_error(e, "hipEventRecord (staging)");
+  if (e != hipSuccess) {
+    // Without the event the slot's copy cannot be tracked: let it finish
+    // before the slot can be filled again.
+    (void)hipStreamSynchronize(stream);
+    return hip_error(e, "hipEventRecord (staging)");
+  }
   s.pending = true;
   return HKV_OK;
 }
