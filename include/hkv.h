@@ -223,8 +223,12 @@ typedef struct hkv_chunk_batch {
                                 pages are whole or null. */
 } hkv_chunk_batch;
 
-/* Device workspace bytes needed by a call with up to max_chunks chunks.
- * Errors: HKV_E_ARG. */
+/* Device workspace bytes needed by a call with up to max_chunks chunks: the
+ * call's tables (layer placements, work items, block ids, object addresses,
+ * token counts), with room for up to 8 per-class item lists.  A retrieve
+ * with null ids or partial chunks whose chunks fall into at most 8 classes
+ * (same null entries, same token count) launches once per class over only
+ * the work items that write something.  Errors: HKV_E_ARG. */
 hkv_status hkv_workspace_size(const hkv_layout* layout, int32_t max_chunks, size_t* bytes);
 
 /* Store (gather): for every chunk c, layer l and block j < k, copies the

@@ -7,7 +7,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhkv.so")
 
-SOURCES = ["hkv_plan.cpp", "hkv_keys.cpp", "hkv_api.cpp", "hkv_copy.hip"]
+SOURCES = ["hkv_plan.cpp", "hkv_groups.cpp", "hkv_keys.cpp", "hkv_api.cpp", "hkv_copy.hip"]
 # The INT8 codec takes integer decisions in fp32 on both the GPU and the CPU
 # oracle: keep IEEE division and fp32 denormals explicit.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",

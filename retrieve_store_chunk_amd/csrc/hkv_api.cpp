@@ -18,6 +18,7 @@
 
 #include "hkv.h"
 #include "hkv_device_tables.hpp"
+#include "hkv_groups.hpp"
 #include "hkv_launch.hpp"
 #include "hkv_plan.hpp"
 
@@ -144,6 +145,62 @@ hkv_status check_disjoint(std::vector<Span>& spans) {
   return HKV_OK;
 }
 
+// ---------------------------------------------------------------- launches
+// Fills the kernel arguments for one launch over `n` chunks whose tables sit
+// at the given workspace offsets, and enqueues it.
+hkv_status launch_one(bool store, const hkv::Plan& p, const void* pool, uint8_t* wsb,
+                      uint64_t layers_off, uint64_t items_off, uint64_t n_items,
+                      uint64_t ids_off, uint64_t objs_off, uint64_t tokens_off,
+                      bool has_tokens, uint64_t n, void* stream) {
+  if (n == 0 || n_items == 0) return HKV_OK;
+  hkv::CopyArgs a{};
+  a.pool = static_cast<uint8_t*>(const_cast<void*>(pool));
+  a.layers = reinterpret_cast<const hkv::DevLayer*>(wsb + layers_off);
+  a.items = reinterpret_cast<const uint64_t*>(wsb + items_off);
+  a.ids = reinterpret_cast<const int32_t*>(wsb + ids_off);
+  a.objs = reinterpret_cast<const uint64_t*>(wsb + objs_off);
+  a.chunk_tokens = has_tokens ? reinterpret_cast<const int32_t*>(wsb + tokens_off) : nullptr;
+  a.total_items = n * n_items;
+  a.block_tokens = (uint64_t)p.block_size;
+  a.tile_bytes = p.tile_bytes;
+  a.codec_rows_per_item = p.codec_rows_per_item;
+  a.items_per_chunk = (uint32_t)n_items;
+  a.n_kv_groups = (uint32_t)p.n_kv_groups;
+  a.blocks_per_chunk = (uint32_t)p.blocks_per_chunk;
+  a.n_obj_groups = (uint32_t)p.n_obj_groups;
+  // One workgroup per tile, unless capped by the caller or by the 32-bit
+  // grid size (workgroups x threads); workgroups then loop over tiles.
+  uint64_t grid = a.total_items;
+  if (p.max_workgroups && grid > p.max_workgroups) grid = p.max_workgroups;
+  const uint64_t grid_limit = 0xFFFFFFFFull / hkv::kCopyThreads;
+  if (grid > grid_limit) grid = grid_limit;
+  const int e = hkv::launch_copy(store, a, (uint32_t)grid, stream);
+  if (e != 0)
+    return hip_error((hipError_t)e, store ? "launching hkv_store_gather"
+                                          : "launching hkv_retrieve_scatter");
+  return HKV_OK;
+}
+
+// The grouped retrieve (hkv_groups.hpp): one upload of every class's tables,
+// then one launch per class.  Sets *done when it took the call.
+hkv_status retrieve_grouped(const hkv::Plan& p, const void* pool, const hkv_chunk_batch* b,
+                            void* ws, void* stream, bool* done) {
+  hkv::GroupedCall g;
+  *done = hkv::plan_grouped_retrieve(p, *b, &g);
+  if (!*done || g.launches.empty()) return HKV_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hkv_status st =
+      upload(ws, g.ws.total, s, [&](uint8_t* h) { hkv::fill_grouped_tables(p, *b, g, h); });
+  if (st != HKV_OK) return st;
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  for (const hkv::GroupLaunch& L : g.launches) {
+    st = launch_one(false, p, pool, wsb, g.ws.layers_off, L.items_off, L.n_items, L.ids_off,
+                    L.objs_off, L.tokens_off, b->chunk_tokens != nullptr, L.n_chunks, stream);
+    if (st != HKV_OK) return st;
+  }
+  return HKV_OK;
+}
+
 hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
                     const hkv_chunk_batch* b, void* ws, size_t ws_bytes, void* stream) {
   if (!layout || !b) return set_error(HKV_E_ARG, "layout and batch must not be NULL");
@@ -160,8 +217,11 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
     return set_error(HKV_E_ARG, "too many tiles in one call; split the batch");
   const hkv::WorkspaceLayout wl =
       hkv::workspace_layout(p.dev_layers.size(), per_chunk, n, G, k, O);
-  if (!ws || ws_bytes < wl.total)
-    return set_error(HKV_E_WORKSPACE, "workspace needs " + std::to_string(wl.total) + " bytes");
+  // What hkv_workspace_size(n) promises: room for the grouped retrieve too.
+  const uint64_t ws_need =
+      std::max(wl.total, hkv::grouped_layout(p, hkv::kMaxCallGroups * per_chunk, n).total);
+  if (!ws || ws_bytes < ws_need)
+    return set_error(HKV_E_WORKSPACE, "workspace needs " + std::to_string(ws_need) + " bytes");
   if (!aligned16(pool)) return set_error(HKV_E_ALIGN, "pool pointer is not 16-byte aligned");
   if (!aligned16(ws)) return set_error(HKV_E_ALIGN, "workspace is not 16-byte aligned");
   for (uint64_t i = 0; i < n * O; ++i) {
@@ -198,7 +258,7 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   const uintptr_t pb = reinterpret_cast<uintptr_t>(pool);
   spans.push_back({pb, pb + p.pool_used, "the pool"});
   const uintptr_t wb = reinterpret_cast<uintptr_t>(ws);
-  spans.push_back({wb, wb + wl.total, "the workspace"});
+  spans.push_back({wb, wb + ws_need, "the workspace"});
   for (uint64_t c = 0; c < n; ++c)
     for (uint64_t o = 0; o < O; ++o) {
       const uintptr_t a = reinterpret_cast<uintptr_t>(b->objects[c * O + o]);
@@ -207,8 +267,17 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   hkv_status st = check_disjoint(spans);
   if (st != HKV_OK) return st;
 
+  if (!store) {
+    bool any_null = false;
+    for (uint64_t i = 0; i < n_ids && !any_null; ++i) any_null = ids[i] == HKV_NULL_BLOCK;
+    if (any_null || b->chunk_tokens) {
+      bool done = false;
+      st = retrieve_grouped(p, pool, b, ws, stream, &done);
+      if (st != HKV_OK || done) return st;
+    }
+  }
+
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  uint8_t* wsb = static_cast<uint8_t*>(ws);
   st = upload(ws, wl.total, s, [&](uint8_t* h) {
     std::memcpy(h + wl.layers_off, p.dev_layers.data(), p.dev_layers.size() * sizeof(hkv::DevLayer));
     std::memcpy(h + wl.items_off, p.items.data(), per_chunk * sizeof(uint64_t));
@@ -218,33 +287,9 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
     if (b->chunk_tokens) std::memcpy(h + wl.tokens_off, b->chunk_tokens, n * sizeof(int32_t));
   });
   if (st != HKV_OK) return st;
-
-  hkv::CopyArgs a{};
-  a.pool = static_cast<uint8_t*>(const_cast<void*>(pool));
-  a.layers = reinterpret_cast<const hkv::DevLayer*>(wsb + wl.layers_off);
-  a.items = reinterpret_cast<const uint64_t*>(wsb + wl.items_off);
-  a.ids = reinterpret_cast<const int32_t*>(wsb + wl.ids_off);
-  a.objs = reinterpret_cast<const uint64_t*>(wsb + wl.objs_off);
-  a.chunk_tokens =
-      b->chunk_tokens ? reinterpret_cast<const int32_t*>(wsb + wl.tokens_off) : nullptr;
-  a.total_items = n * per_chunk;
-  a.block_tokens = (uint64_t)p.block_size;
-  a.tile_bytes = p.tile_bytes;
-  a.codec_rows_per_item = p.codec_rows_per_item;
-  a.items_per_chunk = (uint32_t)per_chunk;
-  a.n_kv_groups = (uint32_t)G;
-  a.blocks_per_chunk = (uint32_t)k;
-  a.n_obj_groups = (uint32_t)O;
-  // One workgroup per tile, unless capped by the caller or by the 32-bit
-  // grid size (workgroups x threads); workgroups then loop over tiles.
-  uint64_t grid = a.total_items;
-  if (p.max_workgroups && grid > p.max_workgroups) grid = p.max_workgroups;
-  const uint64_t grid_limit = 0xFFFFFFFFull / hkv::kCopyThreads;
-  if (grid > grid_limit) grid = grid_limit;
-  const int e = hkv::launch_copy(store, a, (uint32_t)grid, stream);
-  if (e != 0) return hip_error((hipError_t)e, store ? "launching hkv_store_gather"
-                                                    : "launching hkv_retrieve_scatter");
-  return HKV_OK;
+  return launch_one(store, p, pool, static_cast<uint8_t*>(ws), wl.layers_off, wl.items_off,
+                    per_chunk, wl.ids_off, wl.objs_off, wl.tokens_off, b->chunk_tokens != nullptr,
+                    n, stream);
 }
 
 }  // namespace
@@ -319,11 +364,16 @@ hkv_status hkv_workspace_size(const hkv_layout* layout, int32_t max_chunks, size
   if (!layout || !bytes) return set_error(HKV_E_ARG, "layout and bytes must not be NULL");
   if (max_chunks < 0) return set_error(HKV_E_ARG, "max_chunks must be >= 0");
   const hkv::Plan& p = layout->plan;
-  *bytes = (size_t)hkv::workspace_layout(p.dev_layers.size(), p.items.size(),
-                                         (uint64_t)max_chunks, (uint64_t)p.n_kv_groups,
-                                         (uint64_t)p.blocks_per_chunk,
-                                         (uint64_t)p.n_obj_groups)
-               .total;
+  const uint64_t single = hkv::workspace_layout(p.dev_layers.size(), p.items.size(),
+                                                (uint64_t)max_chunks, (uint64_t)p.n_kv_groups,
+                                                (uint64_t)p.blocks_per_chunk,
+                                                (uint64_t)p.n_obj_groups)
+                              .total;
+  // A retrieve with null ids or partial chunks may use up to kMaxCallGroups
+  // item lists (one per class of chunks).
+  const uint64_t grouped =
+      hkv::grouped_layout(p, hkv::kMaxCallGroups * p.items.size(), (uint64_t)max_chunks).total;
+  *bytes = (size_t)std::max(single, grouped);
   return HKV_OK;
 }
 

@@ -1,0 +1,97 @@
+// Grouped retrieve (see hkv_groups.hpp).  A retrieve writes nothing for a
+// null page and nothing past a partial chunk's last valid row, yet the
+// per-chunk item list launches a workgroup for every tile of every page.
+#include "hkv_groups.hpp"
+
+#include <cstring>
+#include <map>
+
+namespace hkv {
+
+bool plan_grouped_retrieve(const Plan& p, const hkv_chunk_batch& b, GroupedCall* out) {
+  const uint64_t n = (uint64_t)b.n_chunks;
+  const uint64_t G = (uint64_t)p.n_kv_groups, k = (uint64_t)p.blocks_per_chunk;
+  const uint64_t per_chunk = p.items.size();
+  const int32_t* ids = b.block_ids;
+  *out = GroupedCall{};
+  // Class of each chunk: which (group, j) ids are null, and its token count.
+  std::map<std::vector<int32_t>, size_t> class_of;
+  std::vector<std::vector<int32_t>> signature;
+  for (uint64_t c = 0; c < n; ++c) {
+    std::vector<int32_t> sig(G * k + 1);
+    for (uint64_t i = 0; i < G * k; ++i) sig[i] = ids[c * G * k + i] == HKV_NULL_BLOCK;
+    sig[G * k] = b.chunk_tokens ? b.chunk_tokens[c] : -1;
+    auto it = class_of.find(sig);
+    if (it == class_of.end()) {
+      if (out->members.size() == kMaxCallGroups) return false;
+      it = class_of.emplace(sig, out->members.size()).first;
+      out->members.emplace_back();
+      signature.push_back(sig);
+    }
+    out->members[it->second].push_back((uint32_t)c);
+  }
+  // Each class keeps the items of its non-null pages that write at least a
+  // byte, the same test as the kernel's live bytes.
+  out->items.resize(out->members.size());
+  uint64_t n_items_total = 0;
+  for (size_t g = 0; g < out->members.size(); ++g) {
+    const std::vector<int32_t>& sig = signature[g];
+    for (const uint64_t w : p.items) {
+      const uint32_t l = (uint32_t)(w & 0xFFFFu), j = (uint32_t)((w >> 16) & 0xFFFFu);
+      const uint64_t s = (w >> 32) & 0x7FFFFFFFull;
+      const DevLayer& L = p.dev_layers[l];
+      if (sig[L.kv_group * k + j]) continue;  // a null page
+      if ((w >> 63) == 0) {
+        uint64_t valid = L.copy_bytes;
+        if (sig[G * k] >= 0 && L.row_bytes) {
+          int64_t rows = (int64_t)sig[G * k] - (int64_t)j * p.block_size;
+          rows = rows < 0 ? 0 : (rows > p.block_size ? p.block_size : rows);
+          valid = (uint64_t)rows * L.row_bytes;
+        }
+        if (valid <= s * p.tile_bytes) continue;  // past the valid rows
+      }
+      out->items[g].push_back(w);
+    }
+    out->launched_items += out->members[g].size() * out->items[g].size();
+    n_items_total += out->items[g].size();
+  }
+  if (out->launched_items * 10 > n * per_chunk * 9) return false;
+  out->ws = grouped_layout(p, n_items_total, n);
+  const uint64_t O = (uint64_t)p.n_obj_groups;
+  uint64_t item_at = 0, chunk_at = 0;
+  for (size_t g = 0; g < out->members.size(); ++g) {
+    const uint64_t ng = out->members[g].size(), ni = out->items[g].size();
+    if (ni > 0)
+      out->launches.push_back({out->ws.items_off + item_at * sizeof(uint64_t), ni,
+                               out->ws.ids_off + chunk_at * G * k * sizeof(int32_t),
+                               out->ws.objs_off + chunk_at * O * sizeof(uint64_t),
+                               out->ws.tokens_off + chunk_at * sizeof(int32_t), ng});
+    item_at += ni;
+    chunk_at += ng;
+  }
+  return true;
+}
+
+void fill_grouped_tables(const Plan& p, const hkv_chunk_batch& b, const GroupedCall& g,
+                         uint8_t* h) {
+  const uint64_t G = (uint64_t)p.n_kv_groups, k = (uint64_t)p.blocks_per_chunk;
+  const uint64_t O = (uint64_t)p.n_obj_groups;
+  std::memcpy(h + g.ws.layers_off, p.dev_layers.data(), p.dev_layers.size() * sizeof(DevLayer));
+  uint64_t* it = reinterpret_cast<uint64_t*>(h + g.ws.items_off);
+  int32_t* id = reinterpret_cast<int32_t*>(h + g.ws.ids_off);
+  uint64_t* ob = reinterpret_cast<uint64_t*>(h + g.ws.objs_off);
+  int32_t* tk = reinterpret_cast<int32_t*>(h + g.ws.tokens_off);
+  for (size_t c = 0; c < g.members.size(); ++c) {
+    std::memcpy(it, g.items[c].data(), g.items[c].size() * sizeof(uint64_t));
+    it += g.items[c].size();
+    for (const uint32_t ch : g.members[c]) {
+      std::memcpy(id, b.block_ids + (uint64_t)ch * G * k, G * k * sizeof(int32_t));
+      id += G * k;
+      for (uint64_t o = 0; o < O; ++o)
+        *ob++ = reinterpret_cast<uintptr_t>(b.objects[(uint64_t)ch * O + o]);
+      if (b.chunk_tokens) *tk++ = b.chunk_tokens[ch];
+    }
+  }
+}
+
+}  // namespace hkv

@@ -196,6 +196,20 @@ def test_call_validation_on_host():
     assert "workspace" in hkv.hkv_last_error() or hkv.hkv_last_error() != ""
 
 
+def test_calls_past_the_item_limit_are_rejected_before_any_hip_call():
+    """One call covers at most 2^31 - 1 work items (chunks x items per
+    chunk); beyond that the library asks for a split, before it looks at
+    any pointer (so fake addresses are safe here)."""
+    lay = hkv.Layout(workloads.make_config("kl_tp1").desc)
+    per_chunk_items = 14317   # 20 KDA pages of 530 tiles + 7 MLA pages of 531
+    n = (2**31 - 1) // per_chunk_items + 1
+    ids = np.zeros((n, lay.G, lay.k), np.int32)
+    objs = [1 << 40] * (n * lay.O)
+    assert hkv.status_of(hkv.hkv_store_chunks, lay.handle, 1 << 44, ids, objs, 1 << 45,
+                         1 << 40, 0) == hkv.HKV_E_ARG
+    assert "split" in hkv.hkv_last_error()
+
+
 def test_one_hip_runtime_in_the_process():
     """libhkv must bind to the HIP runtime torch uses: two runtimes in one
     process each see the GPU alone (the second reports no device)."""

@@ -166,13 +166,30 @@ def holes_and_tails(cfg, every, tail):
     return cfg
 
 
+def varied_tails(cfg, tails, every=1):
+    """The layout with one request per entry of `tails`, each of two chunks
+    whose second holds that many tokens: the chunks of a retrieve fall into
+    len(set(tails)) + 1 classes."""
+    import copy
+    cfg = copy.deepcopy(cfg)
+    cfg.requests = [2] * len(tails)
+    chunks = W._all_chunks(cfg.requests)
+    tt = {(r, 1): t for r, t in enumerate(tails)}
+    cfg.phases = [W.Phase("store", chunks, False, every, tt),
+                  W.Phase("retrieve", chunks, False, every, tt)]
+    cfg.name += f"_tails{len(set(tails))}"
+    return cfg
+
+
 @pytest.mark.parametrize("cfg", [holes_and_tails(EDGE[0], 2, 5), holes_and_tails(EDGE[1], 1, 1),
                                  holes_and_tails(EDGE[2], 3, 33),
-                                 holes_and_tails(EDGE[9], 2, 17)],
+                                 holes_and_tails(EDGE[9], 2, 17),
+                                 holes_and_tails(EDGE[2], 1, 0)],
                          ids=lambda c: c.name)
 def test_edge_layouts_with_holes_and_tails(cfg):
     """Null ids and partial chunks on odd page sizes (byte path), several
-    blocks per chunk and multi-tile pages (4 KiB tiles)."""
+    blocks per chunk and multi-tile pages (4 KiB tiles); a tail of 0 tokens
+    makes a chunk whose ids are all null."""
     run_parity(cfg)
     run_parity(cfg, tile_bytes=4096, max_workgroups=5)
 
@@ -383,7 +400,8 @@ def test_codec_edge_layouts_and_tuning(cfg, tile, max_wg):
 
 @pytest.mark.parametrize("cfg", [holes_and_tails(CODEC_EDGE[0], 2, 5),
                                  holes_and_tails(CODEC_EDGE[2], 3, 33),
-                                 holes_and_tails(CODEC_EDGE[3], 1, 100)],
+                                 holes_and_tails(CODEC_EDGE[3], 1, 100),
+                                 holes_and_tails(CODEC_EDGE[2], 2, 0)],
                          ids=lambda c: c.name)
 def test_codec_with_holes_and_tails(cfg):
     """Null KDA pages (codes and scales zeroed on store, nothing written on
@@ -394,3 +412,18 @@ def test_codec_with_holes_and_tails(cfg):
 
 def test_codec_host_objects():
     run_parity(W.make_small_config("kl_tp1_int8"), objects="host")
+
+
+@pytest.mark.parametrize("cfg", [varied_tails(mini_config("varied", [0, 1, 0, 1], 1, chunk_min=40,
+                                                           blocks=80), [3, 17, 3, 40, 17, 0]),
+                                 varied_tails(mini_config("varied", [0, 1, 0, 1], 1, chunk_min=40,
+                                                          blocks=240), list(range(1, 40, 3))),
+                                 varied_tails(CODEC_EDGE[2], [5, 33, 5, 0], every=2)],
+                         ids=lambda c: c.name)
+def test_retrieve_classes_and_plain_fallback(cfg):
+    """A retrieve whose chunks fall into a few classes (same null ids, same
+    token count) launches once per class over only the work items that
+    write something; with more than 8 classes it makes one launch over every
+    item.  Both must match the oracle byte for byte."""
+    run_parity(cfg)
+    run_parity(cfg, tile_bytes=4096, max_workgroups=5)
