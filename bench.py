@@ -263,12 +263,13 @@ def main() -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the store/retrieve path has no cross-GPU "
-              "step in this build; run with --gpus 1", file=sys.stderr)
+              "step (each rank stores and retrieves its own shard); run with --gpus 1",
+              file=sys.stderr)
         return 2
 
     import torch
     import workloads as W
-    from workloads.driver import GpuWorkload
+    from workloads.runner import GpuWorkload
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -48,7 +48,7 @@ def _samples(rng, w, n_layers, k, count):
 
 @pytest.mark.parametrize("name", W.CONFIG_NAMES + W.EXTRA_CONFIG_NAMES)
 def test_full_size_sampled(name):
-    from workloads.driver import GpuWorkload
+    from workloads.runner import GpuWorkload
     cfg = W.make_config(name)
     print(f"[fullsize] {name}", flush=True)
     g = GpuWorkload(cfg, objects=cfg.extra.get("objects", "device"))

@@ -30,7 +30,7 @@ def _gpu():
 
 
 def run_parity(cfg, tile_bytes=0, max_workgroups=0, pool_fill=None, objects="device"):
-    from workloads.driver import GpuWorkload
+    from workloads.runner import GpuWorkload
     _log(f"[parity] {cfg.name} tile={tile_bytes} max_wg={max_workgroups} objects={objects}")
     g = GpuWorkload(cfg, tile_bytes=tile_bytes, max_workgroups=max_workgroups, objects=objects)
     ref = oracle.Layout(cfg.desc)
@@ -208,7 +208,7 @@ def test_host_object_parity_edge_layouts(cfg):
 
 def test_empty_batch_is_a_noop():
     import retrieve_store_chunk_amd as hkv
-    from workloads.driver import GpuWorkload
+    from workloads.runner import GpuWorkload
     g = GpuWorkload(W.make_config("tiny"))
     g.init_pool()
     before = g.host_pool().copy()
@@ -222,7 +222,7 @@ def test_empty_batch_is_a_noop():
 
 def test_error_paths_enqueue_nothing():
     import retrieve_store_chunk_amd as hkv
-    from workloads.driver import GpuWorkload
+    from workloads.runner import GpuWorkload
     g = GpuWorkload(W.make_config("tiny"))
     g.init_pool()
     g.fill_objects(5)
@@ -268,7 +268,7 @@ def test_objects_move_between_pool_layouts_with_equal_fingerprints():
     the oracle byte for byte, and storing them again from path A gives the
     same objects."""
     import retrieve_store_chunk_amd as hkv
-    from workloads.driver import GpuWorkload
+    from workloads.runner import GpuWorkload
     cfg_b = W.make_small_config("kl_tp1")
     cfg_a = W.make_small_config("kl_tp1")
     cfg_a.desc = dict(cfg_a.desc, path=0)
