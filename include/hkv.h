@@ -133,8 +133,13 @@ typedef struct hkv_layout_desc {
                                  |x - q s| <= s / 2 for finite x.  Else HKV_E_ARG */
 } hkv_layout_desc;
 
-typedef struct hkv_layout hkv_layout; /* opaque; immutable after init; may be shared by
-                                         threads */
+typedef struct hkv_layout hkv_layout; /* opaque; its plan is immutable after init; may be
+                                         shared by threads.  The first store or retrieve
+                                         on a device copies the plan's constant tables
+                                         (layer placements and per-chunk work items, about
+                                         115 KB at the Kimi-Linear shapes) into that
+                                         device's memory, synchronously; they stay there
+                                         until hkv_layout_destroy. */
 
 /* Plans a layout.  Path A: every layer uses the unified page P = the largest
  * real page (the MLA page), smaller KDA pages are padded to it; slab s holds
@@ -149,8 +154,9 @@ typedef struct hkv_layout hkv_layout; /* opaque; immutable after init; may be sh
  * On success *out owns heap memory released by hkv_layout_destroy. */
 hkv_status hkv_layout_init(const hkv_layout_desc* desc, hkv_layout** out);
 
-/* Releases a layout.  NULL is ignored.  The caller must not destroy a
- * layout while a call that uses it is running on another thread. */
+/* Releases a layout and its tables in device memory.  NULL is ignored.  The
+ * caller must not destroy a layout while a call that uses it is running on
+ * another thread or while work it enqueued has not finished. */
 void hkv_layout_destroy(hkv_layout* layout);
 
 typedef struct hkv_layout_info {
@@ -241,6 +247,11 @@ hkv_status hkv_workspace_size(const hkv_layout* layout, int32_t max_chunks, size
  * 16-byte aligned, ws_bytes >= hkv_workspace_size(n_chunks); it is
  * overwritten and must not be used by another call until the stream passes
  * this one.  stream: a hipStream_t (NULL = the default stream).
+ * The call's block ids, object addresses and token counts travel in the
+ * kernel arguments when they fit in 3 KiB (up to 96 chunks at the
+ * Kimi-Linear shapes), so such a call is a single kernel launch; a larger
+ * call first copies them into the workspace from pinned staging on the
+ * same stream.
  * Repeated source ids are allowed.  Null ids and partial chunks: see
  * HKV_NULL_BLOCK and hkv_chunk_batch.chunk_tokens.
  * Errors: HKV_E_ARG (also a chunk_tokens entry outside [0, C]), HKV_E_RANGE

@@ -24,6 +24,12 @@
 
 struct hkv_layout {
   hkv::Plan plan;
+  // The plan's constant tables (layer placements, then the per-chunk work
+  // items) in the memory of each device the layout has been used on,
+  // uploaded by the first call there and freed with the layout.
+  mutable std::mutex mu;
+  mutable std::map<int, void*> dev_tables;
+  ~hkv_layout();
 };
 
 namespace {
@@ -82,12 +88,18 @@ struct DeviceScope {
   }
 };
 
-// Copies `bytes` bytes of `fill`-written staging into `dst` on `stream`.
+// The device a call's work goes to: the stream's, or the current one for
+// the default stream.
+hkv_status stream_device(hipStream_t stream, int* dev) {
+  const hipError_t e = stream ? hipStreamGetDevice(stream, dev) : hipGetDevice(dev);
+  return e == hipSuccess ? HKV_OK : hip_error(e, "finding the stream's device");
+}
+
+// Copies `bytes` bytes of `fill`-written staging into `dst` on `stream`
+// (whose device is `dev`).
 template <class Fill>
-hkv_status upload(void* dst, size_t bytes, hipStream_t stream, Fill fill) {
-  int dev = 0;
-  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_error(e, "finding the stream's device");
+hkv_status upload(int dev, void* dst, size_t bytes, hipStream_t stream, Fill fill) {
+  hipError_t e = hipSuccess;
   DeviceScope scope(dev);
   if (scope.err != hipSuccess) return hip_error(scope.err, "selecting the stream's device");
   Ring* ring = ring_for(dev);
@@ -145,21 +157,50 @@ hkv_status check_disjoint(std::vector<Span>& spans) {
   return HKV_OK;
 }
 
+// ---------------------------------------------------------------- layout tables
+constexpr uint64_t layer_table_bytes(const hkv::Plan& p) {
+  return hkv::align256(p.dev_layers.size() * sizeof(hkv::DevLayer));
+}
+
+// The layout's constant tables on `dev`: uploaded (synchronously) by the
+// first call there.
+hkv_status layout_tables(const hkv_layout* lay, int dev, const uint8_t** out) {
+  std::lock_guard<std::mutex> g(lay->mu);
+  auto it = lay->dev_tables.find(dev);
+  if (it != lay->dev_tables.end()) {
+    *out = static_cast<const uint8_t*>(it->second);
+    return HKV_OK;
+  }
+  DeviceScope scope(dev);
+  if (scope.err != hipSuccess) return hip_error(scope.err, "selecting the stream's device");
+  const hkv::Plan& p = lay->plan;
+  const uint64_t lb = layer_table_bytes(p), ib = p.items.size() * sizeof(uint64_t);
+  std::vector<uint8_t> h(lb + ib, 0);
+  std::memcpy(h.data(), p.dev_layers.data(), p.dev_layers.size() * sizeof(hkv::DevLayer));
+  std::memcpy(h.data() + lb, p.items.data(), ib);
+  void* d = nullptr;
+  hipError_t e = hipMalloc(&d, lb + ib);
+  if (e != hipSuccess) return hip_error(e, "hipMalloc (layout tables)");
+  e = hipMemcpy(d, h.data(), lb + ib, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(d);
+    return hip_error(e, "hipMemcpy (layout tables)");
+  }
+  lay->dev_tables[dev] = d;
+  *out = static_cast<const uint8_t*>(d);
+  return HKV_OK;
+}
+
 // ---------------------------------------------------------------- launches
-// Fills the kernel arguments for one launch over `n` chunks whose tables sit
-// at the given workspace offsets, and enqueues it.
-hkv_status launch_one(bool store, const hkv::Plan& p, const void* pool, uint8_t* wsb,
-                      uint64_t layers_off, uint64_t items_off, uint64_t n_items,
-                      uint64_t ids_off, uint64_t objs_off, uint64_t tokens_off,
-                      bool has_tokens, uint64_t n, void* stream) {
-  if (n == 0 || n_items == 0) return HKV_OK;
+// Kernel arguments for a launch over `n` chunks of `n_items` items each, with
+// the layer and item tables at `layers` / `items`; the per-call table
+// pointers are left null (inline) for the caller to fill.
+hkv::CopyArgs base_args(const hkv::Plan& p, const void* pool, const uint8_t* layers,
+                        const uint8_t* items, uint64_t n_items, uint64_t n, bool has_tokens) {
   hkv::CopyArgs a{};
   a.pool = static_cast<uint8_t*>(const_cast<void*>(pool));
-  a.layers = reinterpret_cast<const hkv::DevLayer*>(wsb + layers_off);
-  a.items = reinterpret_cast<const uint64_t*>(wsb + items_off);
-  a.ids = reinterpret_cast<const int32_t*>(wsb + ids_off);
-  a.objs = reinterpret_cast<const uint64_t*>(wsb + objs_off);
-  a.chunk_tokens = has_tokens ? reinterpret_cast<const int32_t*>(wsb + tokens_off) : nullptr;
+  a.layers = reinterpret_cast<const hkv::DevLayer*>(layers);
+  a.items = reinterpret_cast<const uint64_t*>(items);
   a.total_items = n * n_items;
   a.block_tokens = (uint64_t)p.block_size;
   a.tile_bytes = p.tile_bytes;
@@ -168,34 +209,49 @@ hkv_status launch_one(bool store, const hkv::Plan& p, const void* pool, uint8_t*
   a.n_kv_groups = (uint32_t)p.n_kv_groups;
   a.blocks_per_chunk = (uint32_t)p.blocks_per_chunk;
   a.n_obj_groups = (uint32_t)p.n_obj_groups;
-  // One workgroup per tile, unless capped by the caller or by the 32-bit
-  // grid size (workgroups x threads); workgroups then loop over tiles.
+  a.has_tokens = has_tokens ? 1u : 0u;
+  return a;
+}
+
+// Enqueues one launch: one workgroup per work item, unless capped by the
+// caller or by the 32-bit grid size (workgroups x threads); workgroups then
+// loop over items.
+hkv_status launch_one(bool store, const hkv::Plan& p, const hkv::CopyArgs& a,
+                      const hkv::InlineTables& t, void* stream) {
+  if (a.total_items == 0) return HKV_OK;
   uint64_t grid = a.total_items;
   if (p.max_workgroups && grid > p.max_workgroups) grid = p.max_workgroups;
   const uint64_t grid_limit = 0xFFFFFFFFull / hkv::kCopyThreads;
   if (grid > grid_limit) grid = grid_limit;
-  const int e = hkv::launch_copy(store, a, (uint32_t)grid, stream);
+  const int e = hkv::launch_copy(store, a, t, (uint32_t)grid, stream);
   if (e != 0)
     return hip_error((hipError_t)e, store ? "launching hkv_store_gather"
                                           : "launching hkv_retrieve_scatter");
   return HKV_OK;
 }
 
+const hkv::InlineTables kNoInlineTables{};
+
 // The grouped retrieve (hkv_groups.hpp): one upload of every class's tables,
 // then one launch per class.  Sets *done when it took the call.
-hkv_status retrieve_grouped(const hkv::Plan& p, const void* pool, const hkv_chunk_batch* b,
-                            void* ws, void* stream, bool* done) {
+hkv_status retrieve_grouped(const hkv::Plan& p, int dev, const void* pool,
+                            const hkv_chunk_batch* b, void* ws, void* stream, bool* done) {
   hkv::GroupedCall g;
   *done = hkv::plan_grouped_retrieve(p, *b, &g);
   if (!*done || g.launches.empty()) return HKV_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hkv_status st =
-      upload(ws, g.ws.total, s, [&](uint8_t* h) { hkv::fill_grouped_tables(p, *b, g, h); });
+  hkv_status st = upload(dev, ws, g.ws.total, s,
+                         [&](uint8_t* h) { hkv::fill_grouped_tables(p, *b, g, h); });
   if (st != HKV_OK) return st;
   uint8_t* wsb = static_cast<uint8_t*>(ws);
+  const bool has_tokens = b->chunk_tokens != nullptr;
   for (const hkv::GroupLaunch& L : g.launches) {
-    st = launch_one(false, p, pool, wsb, g.ws.layers_off, L.items_off, L.n_items, L.ids_off,
-                    L.objs_off, L.tokens_off, b->chunk_tokens != nullptr, L.n_chunks, stream);
+    hkv::CopyArgs a = base_args(p, pool, wsb + g.ws.layers_off, wsb + L.items_off, L.n_items,
+                                L.n_chunks, has_tokens);
+    a.ids = reinterpret_cast<const int32_t*>(wsb + L.ids_off);
+    a.objs = reinterpret_cast<const uint64_t*>(wsb + L.objs_off);
+    a.chunk_tokens = reinterpret_cast<const int32_t*>(wsb + L.tokens_off);
+    st = launch_one(false, p, a, kNoInlineTables, stream);
     if (st != HKV_OK) return st;
   }
   return HKV_OK;
@@ -267,32 +323,56 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   hkv_status st = check_disjoint(spans);
   if (st != HKV_OK) return st;
 
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int dev = 0;
+  st = stream_device(s, &dev);
+  if (st != HKV_OK) return st;
+
   if (!store) {
     bool any_null = false;
     for (uint64_t i = 0; i < n_ids && !any_null; ++i) any_null = ids[i] == HKV_NULL_BLOCK;
     if (any_null || b->chunk_tokens) {
       bool done = false;
-      st = retrieve_grouped(p, pool, b, ws, stream, &done);
+      st = retrieve_grouped(p, dev, pool, b, ws, stream, &done);
       if (st != HKV_OK || done) return st;
     }
   }
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  st = upload(ws, wl.total, s, [&](uint8_t* h) {
-    std::memcpy(h + wl.layers_off, p.dev_layers.data(), p.dev_layers.size() * sizeof(hkv::DevLayer));
-    std::memcpy(h + wl.items_off, p.items.data(), per_chunk * sizeof(uint64_t));
-    std::memcpy(h + wl.ids_off, ids, n_ids * sizeof(int32_t));
-    uint64_t* objs = reinterpret_cast<uint64_t*>(h + wl.objs_off);
+  const uint8_t* tables = nullptr;
+  st = layout_tables(layout, dev, &tables);
+  if (st != HKV_OK) return st;
+  const bool has_tokens = b->chunk_tokens != nullptr;
+  hkv::CopyArgs a =
+      base_args(p, pool, tables, tables + layer_table_bytes(p), per_chunk, n, has_tokens);
+  // Per-call tables: in the kernel arguments when they fit (no copy ahead of
+  // the launch), else uploaded into the workspace.
+  {
+    hkv::InlineTables t;
+    if (hkv::pack_inline_tables(p, *b, &t, &a)) return launch_one(store, p, a, t, stream);
+  }
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  const uint64_t lo = wl.ids_off;  // the per-call sections: ids, objects, tokens
+  st = upload(dev, wsb + lo, wl.total - lo, s, [&](uint8_t* h) {
+    std::memcpy(h + (wl.ids_off - lo), ids, n_ids * sizeof(int32_t));
+    uint64_t* objs = reinterpret_cast<uint64_t*>(h + (wl.objs_off - lo));
     for (uint64_t i = 0; i < n * O; ++i) objs[i] = reinterpret_cast<uintptr_t>(b->objects[i]);
-    if (b->chunk_tokens) std::memcpy(h + wl.tokens_off, b->chunk_tokens, n * sizeof(int32_t));
+    if (has_tokens) std::memcpy(h + (wl.tokens_off - lo), b->chunk_tokens, n * sizeof(int32_t));
   });
   if (st != HKV_OK) return st;
-  return launch_one(store, p, pool, static_cast<uint8_t*>(ws), wl.layers_off, wl.items_off,
-                    per_chunk, wl.ids_off, wl.objs_off, wl.tokens_off, b->chunk_tokens != nullptr,
-                    n, stream);
+  a.ids = reinterpret_cast<const int32_t*>(wsb + wl.ids_off);
+  a.objs = reinterpret_cast<const uint64_t*>(wsb + wl.objs_off);
+  a.chunk_tokens = reinterpret_cast<const int32_t*>(wsb + wl.tokens_off);
+  return launch_one(store, p, a, kNoInlineTables, stream);
 }
 
 }  // namespace
+
+hkv_layout::~hkv_layout() {
+  for (auto& kv : dev_tables) {
+    DeviceScope scope(kv.first);
+    if (scope.err == hipSuccess) (void)hipFree(kv.second);
+  }
+}
 
 extern "C" {
 

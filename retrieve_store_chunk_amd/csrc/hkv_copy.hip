@@ -277,11 +277,20 @@ __device__ __forceinline__ void codec_dispatch(const hkv::CopyArgs& a,
 }
 
 template <bool kStore, uint32_t kUnroll, uint32_t kRun>
-__device__ __forceinline__ void copy_items(const hkv::CopyArgs& a) {
+__device__ __forceinline__ void copy_items(const hkv::CopyArgs& a, const hkv::InlineTables& t) {
   const HKV_CONST hkv::DevLayer* layers = (const HKV_CONST hkv::DevLayer*)a.layers;
   const HKV_CONST uint64_t* items = (const HKV_CONST uint64_t*)a.items;
-  const HKV_CONST int32_t* ids = (const HKV_CONST int32_t*)a.ids;
-  const HKV_CONST uint64_t* objs = (const HKV_CONST uint64_t*)a.objs;
+  // Per-call tables: in the workspace, or in the kernel arguments (which are
+  // read through the constant address space like the workspace tables).
+  const HKV_CONST int32_t* ids =
+      (const HKV_CONST int32_t*)(a.ids ? a.ids
+                                       : reinterpret_cast<const int32_t*>(t.words + a.inline_ids));
+  const HKV_CONST uint64_t* objs =
+      (const HKV_CONST uint64_t*)(a.objs ? a.objs : t.words + a.inline_objs);
+  // (Selected without a null branch: a null alternative makes the compiler
+  // copy the whole argument block to scratch.)  Read only if a.has_tokens.
+  const HKV_CONST int32_t* tokens = (const HKV_CONST int32_t*)(
+      a.chunk_tokens ? a.chunk_tokens : reinterpret_cast<const int32_t*>(t.words + a.inline_tokens));
   const uint32_t total = (uint32_t)a.total_items;
 #if HKV_XCD_REMAP
   // Workgroup b runs on XCD b % 8.
@@ -333,8 +342,8 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a) {
     // Bytes of this span that hold data: all of it, none for a null id, and
     // for an MLA page of a partial chunk the rows of its valid tokens.
     uint64_t valid = id < 0 ? 0 : span;
-    if (a.chunk_tokens && L->row_bytes && id >= 0) {
-      int64_t rows = (int64_t)a.chunk_tokens[c] - (int64_t)j * (int64_t)a.block_tokens;
+    if (a.has_tokens && L->row_bytes && id >= 0) {
+      int64_t rows = (int64_t)tokens[c] - (int64_t)j * (int64_t)a.block_tokens;
       rows = rows < 0 ? 0 : (rows > (int64_t)a.block_tokens ? (int64_t)a.block_tokens : rows);
       valid = (uint64_t)rows * L->row_bytes;
     }
@@ -354,21 +363,22 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a) {
 }  // namespace
 
 extern "C" __global__ __launch_bounds__(kThreads) HKV_OCCUPANCY
-void hkv_store_gather(hkv::CopyArgs a) {
-  copy_items<true, HKV_STORE_UNROLL, HKV_STORE_XCD_RUN>(a);
+void hkv_store_gather(hkv::CopyArgs a, hkv::InlineTables t) {
+  copy_items<true, HKV_STORE_UNROLL, HKV_STORE_XCD_RUN>(a, t);
 }
 
 extern "C" __global__ __launch_bounds__(kThreads) HKV_OCCUPANCY
-void hkv_retrieve_scatter(hkv::CopyArgs a) {
-  copy_items<false, HKV_RETRIEVE_UNROLL, HKV_RETRIEVE_XCD_RUN>(a);
+void hkv_retrieve_scatter(hkv::CopyArgs a, hkv::InlineTables t) {
+  copy_items<false, HKV_RETRIEVE_UNROLL, HKV_RETRIEVE_XCD_RUN>(a, t);
 }
 
 namespace hkv {
 
-int launch_copy(bool store, const CopyArgs& a, uint32_t grid, void* stream) {
+int launch_copy(bool store, const CopyArgs& a, const InlineTables& t, uint32_t grid,
+                void* stream) {
   if (grid == 0) return 0;
   CopyArgs arg = a;
-  void* params[] = {&arg};
+  void* params[] = {&arg, const_cast<InlineTables*>(&t)};
   const void* fn = store ? reinterpret_cast<const void*>(&hkv_store_gather)
                          : reinterpret_cast<const void*>(&hkv_retrieve_scatter);
   return (int)hipLaunchKernel(fn, dim3(grid), dim3(kThreads), params, 0,

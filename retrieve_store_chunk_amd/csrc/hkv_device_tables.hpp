@@ -56,9 +56,9 @@ struct CopyArgs {
   uint8_t* pool;
   const DevLayer* layers;
   const uint64_t* items;   // [items_per_chunk]
-  const int32_t* ids;      // [n_chunks][G][k]
-  const uint64_t* objs;    // [n_chunks][O] device addresses
-  const int32_t* chunk_tokens;  // [n_chunks] valid tokens, or nullptr: all chunks whole
+  const int32_t* ids;      // [n_chunks][G][k], or nullptr: in the InlineTables argument
+  const uint64_t* objs;    // [n_chunks][O] device addresses, or nullptr: inline
+  const int32_t* chunk_tokens;  // [n_chunks] valid tokens, or nullptr: inline (if has_tokens)
   uint64_t total_items;    // n_chunks * items_per_chunk
   uint64_t block_tokens;   // N
   uint64_t tile_bytes;
@@ -67,6 +67,16 @@ struct CopyArgs {
   uint32_t n_kv_groups;
   uint32_t blocks_per_chunk;
   uint32_t n_obj_groups;
+  uint32_t has_tokens;     // 0: every chunk is whole
+  uint32_t inline_ids, inline_objs, inline_tokens;  // word offsets into InlineTables
+};
+
+// A call's block ids, object addresses and token counts, when they fit, travel
+// in the kernel arguments (second argument, by value), so that a small call
+// needs no copy ahead of its launch.
+constexpr uint32_t kInlineWords = 384;  // 3 KiB
+struct InlineTables {
+  uint64_t words[kInlineWords];
 };
 
 // Workspace sections, each starting on a 256-byte boundary.

@@ -94,4 +94,26 @@ void fill_grouped_tables(const Plan& p, const hkv_chunk_batch& b, const GroupedC
   }
 }
 
+bool pack_inline_tables(const Plan& p, const hkv_chunk_batch& b, InlineTables* t, CopyArgs* a) {
+  const uint64_t n = (uint64_t)b.n_chunks;
+  const uint64_t n_ids = n * (uint64_t)p.n_kv_groups * (uint64_t)p.blocks_per_chunk;
+  const uint64_t O = (uint64_t)p.n_obj_groups;
+  const uint64_t id_words = (n_ids * sizeof(int32_t) + 7) / 8, obj_words = n * O;
+  const uint64_t tok_words = b.chunk_tokens ? (n * sizeof(int32_t) + 7) / 8 : 0;
+  if (id_words + obj_words + tok_words > kInlineWords) return false;
+  std::memset(t, 0, sizeof(*t));
+  std::memcpy(t->words, b.block_ids, n_ids * sizeof(int32_t));
+  for (uint64_t i = 0; i < n * O; ++i)
+    t->words[id_words + i] = reinterpret_cast<uintptr_t>(b.objects[i]);
+  if (b.chunk_tokens)
+    std::memcpy(t->words + id_words + obj_words, b.chunk_tokens, n * sizeof(int32_t));
+  a->ids = nullptr;
+  a->objs = nullptr;
+  a->chunk_tokens = nullptr;
+  a->inline_ids = 0;
+  a->inline_objs = (uint32_t)id_words;
+  a->inline_tokens = (uint32_t)(id_words + obj_words);
+  return true;
+}
+
 }  // namespace hkv

@@ -1,6 +1,7 @@
-// Grouped retrieve: the launches of a retrieve whose chunks fall into a few
-// classes (same null ids, same token count), each over only the work items
-// that write something.  Host-only, no HIP.
+// Per-call tables on the host side, no HIP: the grouped retrieve (the
+// launches of a retrieve whose chunks fall into a few classes, same null ids
+// and same token count, each over only the work items that write something)
+// and the packing of a small call's tables into the kernel arguments.
 #pragma once
 
 #include <cstdint>
@@ -45,5 +46,10 @@ bool plan_grouped_retrieve(const Plan& p, const hkv_chunk_batch& b, GroupedCall*
 // Writes the grouped call's tables (out->ws layout, ws.total bytes) to `h`.
 void fill_grouped_tables(const Plan& p, const hkv_chunk_batch& b, const GroupedCall& g,
                          uint8_t* h);
+
+// Packs the call's block ids, object addresses and token counts into `t` and
+// sets a's inline offsets, if they fit in kInlineWords words; returns false
+// (nothing written) otherwise.
+bool pack_inline_tables(const Plan& p, const hkv_chunk_batch& b, InlineTables* t, CopyArgs* a);
 
 }  // namespace hkv

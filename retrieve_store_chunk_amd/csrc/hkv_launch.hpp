@@ -14,7 +14,9 @@ constexpr uint32_t kCopyThreads = HKV_THREADS;
 
 // Enqueues the gather (store) or scatter (retrieve) kernel over
 // a.total_items work items with `grid` workgroups on `stream` (a
-// hipStream_t).  Returns the hipError_t of the launch (0 = success).
-int launch_copy(bool store, const CopyArgs& a, uint32_t grid, void* stream);
+// hipStream_t); `t` carries the per-call tables that a leaves null.
+// Returns the hipError_t of the launch (0 = success).
+int launch_copy(bool store, const CopyArgs& a, const InlineTables& t, uint32_t grid,
+                void* stream);
 
 }  // namespace hkv
