@@ -427,3 +427,28 @@ def test_retrieve_classes_and_plain_fallback(cfg):
     item.  Both must match the oracle byte for byte."""
     run_parity(cfg)
     run_parity(cfg, tile_bytes=4096, max_workgroups=5)
+
+
+def call_size_config(n, tails):
+    """n one-chunk requests of a two-group layout, all in one call: 3 words of
+    per-call tables a chunk (ids, two object addresses), plus half a word
+    with token counts, against 384 words of kernel arguments."""
+    import copy
+    cfg = mini_config(f"calls{n}", [0, 1], 1, blocks=2 * n + 8, requests=(1,) * n)
+    cfg = copy.deepcopy(cfg)
+    chunks = W._all_chunks(cfg.requests)
+    tt = {(r, 0): 1 + r % 15 for r in range(n)} if tails else {}
+    cfg.phases = [W.Phase("store", chunks, False, 1, tt), W.Phase("retrieve", chunks, False, 1, tt)]
+    cfg.name += "_tails" if tails else ""
+    return cfg
+
+
+@pytest.mark.parametrize("n,tails", [(128, False), (129, False), (109, True), (110, True)])
+def test_calls_at_the_kernel_argument_limit(n, tails):
+    """A call whose per-call tables fit in the kernel arguments (128 chunks
+    here, 109 with token counts) is one launch; one chunk more goes through
+    the workspace.  Both sides of the limit match the oracle."""
+    cfg = call_size_config(n, tails)
+    ref = oracle.Layout(cfg.desc)
+    assert (ref.G, ref.k, ref.O) == (2, 1, 2)
+    run_parity(cfg)
