@@ -293,29 +293,7 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a, const hkv::In
       a.chunk_tokens ? a.chunk_tokens : reinterpret_cast<const int32_t*>(t.words + a.inline_tokens));
   const uint32_t total = (uint32_t)a.total_items;
 #if HKV_XCD_REMAP
-  // Workgroup b runs on XCD b % 8.
-  const uint32_t x = blockIdx.x % kXcds;
-  uint32_t first;
-  if (kRun == 0) {
-    // XCD x takes the contiguous item range [x*q + min(x, r), ...) of this
-    // round, so one XCD works through whole pages.
-    const uint32_t q = gridDim.x / kXcds, r = gridDim.x % kXcds;
-    first = x * q + (x < r ? x : r) + blockIdx.x / kXcds;
-  } else {
-    // In each span of 8 runs of kRun items XCD x takes run x, in order, so
-    // the XCDs work side by side on neighbouring runs; the last partial span
-    // is split into one contiguous range per XCD.
-    const uint32_t run = kRun ? kRun : 1;
-    const uint32_t full = gridDim.x / (kXcds * run) * (kXcds * run);
-    if (blockIdx.x < full) {
-      const uint32_t j = blockIdx.x / kXcds;
-      first = (j / run) * (kXcds * run) + x * run + (j % run);
-    } else {
-      const uint32_t t = blockIdx.x - full, n = gridDim.x - full;
-      const uint32_t q = n / kXcds, r = n % kXcds;
-      first = full + x * q + (x < r ? x : r) + t / kXcds;
-    }
-  }
+  const uint32_t first = hkv::xcd_first_item(blockIdx.x, gridDim.x, kRun, kXcds);
 #else
   const uint32_t first = blockIdx.x;
 #endif

@@ -51,6 +51,31 @@ inline constexpr uint32_t codec_lanes_per_row(uint32_t head_dim) {
                                                 : head_dim / (4 * HKV_CODEC_VECS);
 }
 
+// The work item that workgroup b of a grid of `grid` workgroups takes first
+// (it then strides by `grid`).  Workgroup b runs on XCD b % xcds.
+//   run == 0: XCD x takes one contiguous range of the items, so the
+//             workgroups of an XCD sweep a narrow window of pages;
+//   run > 0:  in each span of xcds runs of `run` items XCD x takes run x, in
+//             order, so the XCDs work side by side on neighbouring runs; the
+//             last partial span is split into one contiguous range per XCD.
+// Either way the map is a bijection of [0, grid).
+inline constexpr uint32_t xcd_first_item(uint32_t b, uint32_t grid, uint32_t run,
+                                         uint32_t xcds) {
+  const uint32_t x = b % xcds;
+  if (run == 0) {
+    const uint32_t q = grid / xcds, r = grid % xcds;
+    return x * q + (x < r ? x : r) + b / xcds;
+  }
+  const uint32_t full = grid / (xcds * run) * (xcds * run);
+  if (b < full) {
+    const uint32_t j = b / xcds;
+    return (j / run) * (xcds * run) + x * run + (j % run);
+  }
+  const uint32_t t = b - full, n = grid - full;
+  const uint32_t q = n / xcds, r = n % xcds;
+  return full + x * q + (x < r ? x : r) + t / xcds;
+}
+
 // Kernel argument block (passed by value).
 struct CopyArgs {
   uint8_t* pool;
