@@ -452,3 +452,56 @@ def test_calls_at_the_kernel_argument_limit(n, tails):
     ref = oracle.Layout(cfg.desc)
     assert (ref.G, ref.k, ref.O) == (2, 1, 2)
     run_parity(cfg)
+
+
+def random_layout_cases(n_cases=100, seed=2026):
+    """Seeded random small layouts: layer pattern, head count and head_dim,
+    conv and MLA widths and dtypes, path, object grouping, chunk minimum, the
+    INT8 codec where the shape allows it, snapshot spacing, tails and tuning.
+    Cases the oracle rejects are redrawn."""
+    import copy
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n_cases:
+        n_layers = int(rng.integers(1, 7))
+        is_mla = [int(x) for x in rng.integers(0, 2, n_layers)]
+        heads = int(rng.integers(1, 4))
+        head_dim = int(rng.choice([4, 8, 16, 32, 64]))
+        conv_dim = int(rng.choice([0, 4, 5, 8, 24]))
+        mla_width = int(rng.choice([8, 9, 64, 576]))
+        mla_bytes = int(rng.choice([1, 2]))
+        codec = int(head_dim >= 16 and (conv_dim * 3 * 2) % 16 == 0 and rng.random() < 0.5)
+        desc = W._desc(is_mla, heads, head_dim, conv_dim, mla_bytes, int(rng.integers(0, 2)),
+                       1 << 30, chunk_min=int(rng.integers(1, 60)),
+                       separate=int(rng.integers(0, 2)), mla_width=mla_width, kda_codec=codec)
+        try:
+            probe = oracle.Layout(desc)
+        except oracle.OracleError:
+            continue
+        s = probe.summary
+        per_block = s["pool_bytes_used"] // s["num_blocks"]
+        requests = [int(x) for x in rng.integers(1, 4, int(rng.integers(1, 5)))]
+        ids_needed = sum(requests) * probe.G * probe.k
+        desc["pool_bytes"] = (ids_needed + int(rng.integers(0, 6))) * per_block + 7
+        every = int(rng.choice([1, 1, 2, 3]))
+        tails = {}
+        if rng.random() < 0.5:
+            tails = {(r, n - 1): int(rng.integers(0, s["chunk_tokens"] + 1))
+                     for r, n in enumerate(requests)}
+        chunks = W._all_chunks(requests)
+        name = f"rand{len(cases)}"
+        cfg = W.Config(name, name, desc, requests,
+                       [W.Phase("store", chunks, False, every, tails),
+                        W.Phase("retrieve", chunks, False, every, tails)],
+                       seed=W.derive_seed(seed, len(cases)))
+        tile = int(rng.choice([0, 4096, 8192, 1 << 20]))
+        max_wg = int(rng.choice([0, 0, 1, 5, 64]))
+        cases.append((cfg, tile, max_wg))
+    return cases
+
+
+@pytest.mark.parametrize("case", random_layout_cases(), ids=lambda c: c[0].name)
+def test_random_layouts(case):
+    """Random small layouts, byte for byte against the oracle."""
+    cfg, tile, max_wg = case
+    run_parity(cfg, tile_bytes=tile, max_workgroups=max_wg)
