@@ -197,11 +197,14 @@ def hbm_ceiling(buf, stream, reps: int = 10) -> dict:
 
 
 def host_link_ceiling(stream, reps: int = 3) -> dict:
-    """DMA copies of 4 GiB between pinned host memory and HBM (torch copy_)."""
+    """DMA copies of 4 GiB between pinned host memory and HBM (torch copy_):
+    each direction alone, then both at once on two streams."""
     import torch
     n = 4 << 30
     dev = torch.empty(n, dtype=torch.uint8, device="cuda")
     host = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    dev2 = torch.empty(n, dtype=torch.uint8, device="cuda")
+    host2 = torch.empty(n, dtype=torch.uint8, pin_memory=True)
     res = {"bytes": n}
     with torch.cuda.stream(stream):
         for name, fn in (("device_to_host", lambda: host.copy_(dev, non_blocking=True)),
@@ -214,7 +217,17 @@ def host_link_ceiling(stream, reps: int = 3) -> dict:
             e1.record(stream)
             e1.synchronize()
             res[name + "_GBs"] = round(n / (e0.elapsed_time(e1) / reps / 1e3) / 1e9, 1)
-    del dev, host
+    other = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        with torch.cuda.stream(stream):
+            host.copy_(dev, non_blocking=True)
+        with torch.cuda.stream(other):
+            dev2.copy_(host2, non_blocking=True)
+    torch.cuda.synchronize()
+    res["both_directions_GBs"] = round(2 * n * reps / (time.perf_counter() - t0) / 1e9, 1)
+    del dev, host, dev2, host2
     return res
 
 
@@ -246,8 +259,12 @@ def main() -> int:
     ap.add_argument("--config", default="kl_tp1",
                     help="workload: tiny, kl_tp2, kl_tp1 (default), k3_tp8, long_ctx, "
                          "kl_tp1_host (objects in pinned host memory), k3_tp8_holes, "
-                         "kl_tp1_tails, kl_tp1_int8 (INT8 KDA objects)")
+                         "kl_tp1_tails, kl_tp1_int8 (INT8 KDA objects), kl_tp1_host_duplex "
+                         "(host objects, a store and a retrieve at once on two streams)")
     ap.add_argument("--tile-bytes", type=int, default=0)
+    ap.add_argument("--retrieve-engine", choices=("kernel", "dma"), default=None,
+                    help="retrieves by the scatter kernel or by DMA copies of page runs "
+                         "(default: the workload's choice, else the kernel)")
     ap.add_argument("--max-workgroups", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-ceiling", action="store_true",
@@ -278,7 +295,7 @@ def main() -> int:
     log(f"workload {cfg.name}: {cfg.title}")
     objects_on = cfg.extra.get("objects", "device")
     g = GpuWorkload(cfg, tile_bytes=args.tile_bytes, max_workgroups=args.max_workgroups,
-                    objects=objects_on)
+                    objects=objects_on, retrieve_engine=args.retrieve_engine)
     info = g.info
     log(f"layout: N={info['block_size']} C={info['chunk_tokens']} k={info['blocks_per_chunk']} "
         f"blocks={info['num_blocks']} stride={info['block_stride']} "
@@ -307,12 +324,13 @@ def main() -> int:
     step_hbm = sum(per_wave_hbm)
 
     def one_step(events=None):
+        # a duplex workload's retrieves run on a second stream, beside its stores
         for i, w in enumerate(g.waves):
             if events is not None:
-                events[i][0].record(stream)
+                events[i][0].record(g.stream_of(w))
             g.run_wave(w)
             if events is not None:
-                events[i][1].record(stream)
+                events[i][1].record(g.stream_of(w))
 
     for _ in range(args.warmup):
         one_step()
@@ -334,7 +352,8 @@ def main() -> int:
     # per-kernel: each call enqueues one tiny table upload and one launch
     kern = {}
     for i, w in enumerate(g.waves):
-        name = "hkv_store_gather" if w.op == "store" else "hkv_retrieve_scatter"
+        name = ("hkv_store_gather" if w.op == "store" else
+                "retrieve_dma_copies" if g.retrieve_engine else "hkv_retrieve_scatter")
         ms = [evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]
         k = kern.setdefault(name, {"launches": 0, "ms": 0.0, "hbm": 0, "link": 0})
         k["launches"] += args.steps
@@ -358,7 +377,14 @@ def main() -> int:
                              "hbm_GBs": round(hbm / (avg_ms / 1e3) / 1e9, 1)}
     unit_key = "link_bytes_per_launch" if on_host else "hbm_bytes_per_launch"
     dom = max(kernels, key=lambda n: kernels[n][unit_key] * kernels[n]["launches_per_step"])
-    if on_host:
+    link_peak = HOST_LINK_PEAK_GBS * (2 if g.duplex else 1)  # the link is full duplex
+    if on_host and g.duplex:
+        # both directions at once: the link bytes of a step over its time
+        achieved = round(sum(per_wave_link) / (ms_per_step / 1e3) / 1e9, 2)
+        roofline = {"bound": "host-link", "kernel": "hkv_store_gather + hkv_retrieve_scatter "
+                    "(concurrent)", "achieved": achieved, "peak": link_peak, "unit": "GB/s",
+                    "frac": round(achieved / link_peak, 4), "traffic": None}
+    elif on_host:
         achieved = kernels[dom]["link_GBs"]
         roofline = {"bound": "host-link", "kernel": dom, "achieved": achieved,
                     "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
@@ -390,11 +416,12 @@ def main() -> int:
                    "hbm_bytes_per_step": step_hbm,
                    "block_size": info["block_size"], "chunk_tokens": info["chunk_tokens"],
                    "path": "B packed" if info["path"] else "A padded-unified",
-                   "tile_bytes": args.tile_bytes, "max_workgroups": args.max_workgroups},
+                   "tile_bytes": args.tile_bytes, "max_workgroups": args.max_workgroups,
+                   "retrieve_engine": "dma" if g.retrieve_engine else "kernel"},
         "objects": objects_on,
         "pct_hbm_peak": None if on_host else
         round(100 * step_hbm / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
-        "pct_host_link_peak": round(100 * value / HOST_LINK_PEAK_GBS, 2) if on_host else None,
+        "pct_host_link_peak": round(100 * value / link_peak, 2) if on_host else None,
         "chunks_per_s": round(sum(len(w.chunks) for w in g.waves) / (ms_per_step / 1e3), 1),
         "kernels": kernels,
         "roofline": roofline,

@@ -227,7 +227,21 @@ typedef struct hkv_chunk_batch {
                                 (j+1)*N)) only; store zeroes the rest of that page's
                                 object bytes and retrieve writes only those rows.  KDA
                                 pages are whole or null. */
+  int32_t engine;            /* HKV_ENGINE_KERNEL (0): the gather/scatter kernels.
+                                HKV_ENGINE_DMA (1), retrieve only: the pages go by DMA
+                                copies on the stream (hipMemcpyAsync), one per run of
+                                pages that are contiguous in both the object and the pool
+                                (a path B KV group's pages of one block are one run).
+                                For chunk objects in pinned host memory this leaves the
+                                host link's other direction and the compute units to a
+                                concurrent store (LMCache keeps objects in a pinned host
+                                L1: "Kimi-Linear" and "Kimi K3" recipes).  Not for INT8
+                                layouts (the codec decodes in the scatter kernel) or
+                                stores (they zero-fill object bytes): HKV_E_ARG. */
 } hkv_chunk_batch;
+
+#define HKV_ENGINE_KERNEL 0
+#define HKV_ENGINE_DMA 1
 
 /* Device workspace bytes needed by a call with up to max_chunks chunks: the
  * call's tables (layer placements, work items, block ids, object addresses,

@@ -68,7 +68,12 @@ HKV_NULL_BLOCK = -1
 
 class hkv_chunk_batch(ctypes.Structure):
     _fields_ = [("n_chunks", i32), ("block_ids", ctypes.POINTER(i32)),
-                ("objects", ctypes.POINTER(vp)), ("chunk_tokens", ctypes.POINTER(i32))]
+                ("objects", ctypes.POINTER(vp)), ("chunk_tokens", ctypes.POINTER(i32)),
+                ("engine", i32)]
+
+
+HKV_ENGINE_KERNEL = 0
+HKV_ENGINE_DMA = 1
 
 
 def one_hip_runtime() -> None:
@@ -233,11 +238,11 @@ def hkv_chunk_keys(handle: int, tokens, hash_block_tokens: int = 0, root: int = 
     return prefix[:n_fine], keys[:got.value]
 
 
-def _batch(handle, block_ids, objects, info=None, chunk_tokens=None):
+def _batch(handle, block_ids, objects, info=None, chunk_tokens=None, engine=HKV_ENGINE_KERNEL):
     """block_ids: int32 array [n][G][k]; objects: flat sequence of n*O device
-    addresses (chunk-major); chunk_tokens: None or int32 [n].  Shapes are
-    checked against the layout so the library never reads past the host
-    arrays."""
+    addresses (chunk-major); chunk_tokens: None or int32 [n]; engine:
+    HKV_ENGINE_KERNEL or HKV_ENGINE_DMA.  Shapes are checked against the
+    layout so the library never reads past the host arrays."""
     import numpy as np
     ids = np.ascontiguousarray(block_ids, dtype=np.int32)
     n = int(ids.shape[0]) if ids.ndim else 0
@@ -257,14 +262,15 @@ def _batch(handle, block_ids, objects, info=None, chunk_tokens=None):
     addrs = (vp * max(1, len(objects)))(*[int(a) for a in objects])
     b = hkv_chunk_batch(n, ids.ctypes.data_as(ctypes.POINTER(i32)),
                         ctypes.cast(addrs, ctypes.POINTER(vp)),
-                        None if toks is None else toks.ctypes.data_as(ctypes.POINTER(i32)))
+                        None if toks is None else toks.ctypes.data_as(ctypes.POINTER(i32)),
+                        int(engine))
     return b, (ids, addrs, toks)
 
 
 def hkv_store_chunks(handle: int, pool_ptr: int, block_ids, objects, workspace_ptr: int,
                      ws_bytes: int, stream: int = 0, info: dict | None = None,
-                     chunk_tokens=None) -> None:
-    b, keep = _batch(handle, block_ids, objects, info, chunk_tokens)
+                     chunk_tokens=None, engine: int = HKV_ENGINE_KERNEL) -> None:
+    b, keep = _batch(handle, block_ids, objects, info, chunk_tokens, engine)
     _check(lib.hkv_store_chunks(handle, pool_ptr, ctypes.byref(b), workspace_ptr, ws_bytes,
                                 stream), "hkv_store_chunks")
     del keep
@@ -272,8 +278,8 @@ def hkv_store_chunks(handle: int, pool_ptr: int, block_ids, objects, workspace_p
 
 def hkv_retrieve_chunks(handle: int, pool_ptr: int, block_ids, objects, workspace_ptr: int,
                         ws_bytes: int, stream: int = 0, info: dict | None = None,
-                        chunk_tokens=None) -> None:
-    b, keep = _batch(handle, block_ids, objects, info, chunk_tokens)
+                        chunk_tokens=None, engine: int = HKV_ENGINE_KERNEL) -> None:
+    b, keep = _batch(handle, block_ids, objects, info, chunk_tokens, engine)
     _check(lib.hkv_retrieve_chunks(handle, pool_ptr, ctypes.byref(b), workspace_ptr, ws_bytes,
                                    stream), "hkv_retrieve_chunks")
     del keep
@@ -327,11 +333,11 @@ class Layout:
                               info=self.info)
 
     def store(self, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream=0,
-              chunk_tokens=None):
+              chunk_tokens=None, engine=HKV_ENGINE_KERNEL):
         hkv_store_chunks(self.handle, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream,
-                         info=self.info, chunk_tokens=chunk_tokens)
+                         info=self.info, chunk_tokens=chunk_tokens, engine=engine)
 
     def retrieve(self, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream=0,
-                 chunk_tokens=None):
+                 chunk_tokens=None, engine=HKV_ENGINE_KERNEL):
         hkv_retrieve_chunks(self.handle, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream,
-                            info=self.info, chunk_tokens=chunk_tokens)
+                            info=self.info, chunk_tokens=chunk_tokens, engine=engine)

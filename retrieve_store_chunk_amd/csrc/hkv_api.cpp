@@ -265,6 +265,14 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   if (!pool || !b->block_ids || !b->objects)
     return set_error(HKV_E_ARG, "pool, block_ids and objects must not be NULL");
   const hkv::Plan& p = layout->plan;
+  if (b->engine != HKV_ENGINE_KERNEL && b->engine != HKV_ENGINE_DMA)
+    return set_error(HKV_E_ARG, "engine must be HKV_ENGINE_KERNEL or HKV_ENGINE_DMA");
+  if (b->engine == HKV_ENGINE_DMA && store)
+    return set_error(HKV_E_ARG, "the DMA engine serves retrieves only (a store zero-fills "
+                                "object bytes)");
+  if (b->engine == HKV_ENGINE_DMA && p.kda_codec)
+    return set_error(HKV_E_ARG, "the DMA engine copies bytes; an INT8 layout retrieves "
+                                "through the scatter kernel, which decodes");
   const uint64_t n = (uint64_t)b->n_chunks;
   const uint64_t G = (uint64_t)p.n_kv_groups, k = (uint64_t)p.blocks_per_chunk;
   const uint64_t O = (uint64_t)p.n_obj_groups;
@@ -327,6 +335,21 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   int dev = 0;
   st = stream_device(s, &dev);
   if (st != HKV_OK) return st;
+
+  if (b->engine == HKV_ENGINE_DMA) {
+    // One copy per run of pages contiguous in both the object and the pool.
+    std::vector<hkv::DmaRun> runs;
+    hkv::plan_dma_runs(p, *b, reinterpret_cast<uintptr_t>(pool), &runs);
+    DeviceScope scope(dev);
+    if (scope.err != hipSuccess) return hip_error(scope.err, "selecting the stream's device");
+    for (const hkv::DmaRun& r : runs) {
+      const hipError_t e = hipMemcpyAsync(reinterpret_cast<void*>(r.dst),
+                                          reinterpret_cast<const void*>(r.src), r.bytes,
+                                          hipMemcpyDefault, s);
+      if (e != hipSuccess) return hip_error(e, "hipMemcpyAsync (DMA retrieve)");
+    }
+    return HKV_OK;
+  }
 
   if (!store) {
     bool any_null = false;

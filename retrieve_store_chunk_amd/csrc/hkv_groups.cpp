@@ -116,4 +116,44 @@ bool pack_inline_tables(const Plan& p, const hkv_chunk_batch& b, InlineTables* t
   return true;
 }
 
+void plan_dma_runs(const Plan& p, const hkv_chunk_batch& b, uint64_t pool,
+                   std::vector<DmaRun>* out) {
+  out->clear();
+  const uint64_t G = (uint64_t)p.n_kv_groups, k = (uint64_t)p.blocks_per_chunk;
+  const uint64_t O = (uint64_t)p.n_obj_groups, N = (uint64_t)p.block_size;
+  for (uint64_t c = 0; c < (uint64_t)b.n_chunks; ++c) {
+    const int64_t t = b.chunk_tokens ? b.chunk_tokens[c] : (int64_t)(N * k);
+    for (uint64_t o = 0; o < O; ++o) {
+      const uint64_t obj = reinterpret_cast<uintptr_t>(b.objects[c * O + o]);
+      bool open = false;
+      DmaRun run{};
+      for (size_t l = 0; l < p.layers.size(); ++l) {
+        const LayerPlacement& x = p.layers[l];
+        if ((uint64_t)x.obj_group != o) continue;
+        for (uint64_t j = 0; j < k; ++j) {
+          const int32_t id = b.block_ids[(c * G + (uint64_t)x.kv_group) * k + j];
+          if (id == HKV_NULL_BLOCK) continue;
+          uint64_t live = x.page;
+          if (b.chunk_tokens && x.is_mla) {
+            int64_t rows = t - (int64_t)(j * N);
+            rows = rows < 0 ? 0 : (rows > (int64_t)N ? (int64_t)N : rows);
+            live = (uint64_t)rows * (x.page / N);
+          }
+          if (live == 0) continue;
+          const uint64_t src = obj + x.obj_offset + j * x.obj_page;
+          const uint64_t dst = pool + x.pool_offset + (uint64_t)id * x.stride;
+          if (open && run.src + run.bytes == src && run.dst + run.bytes == dst) {
+            run.bytes += live;
+          } else {
+            if (open) out->push_back(run);
+            run = {dst, src, live};
+            open = true;
+          }
+        }
+      }
+      if (open) out->push_back(run);
+    }
+  }
+}
+
 }  // namespace hkv

@@ -1,7 +1,8 @@
-// Per-call tables on the host side, no HIP: the grouped retrieve (the
+// Per-call planning on the host side, no HIP: the grouped retrieve (the
 // launches of a retrieve whose chunks fall into a few classes, same null ids
-// and same token count, each over only the work items that write something)
-// and the packing of a small call's tables into the kernel arguments.
+// and same token count, each over only the work items that write something),
+// the packing of a small call's tables into the kernel arguments, and the
+// copies of a DMA retrieve.
 #pragma once
 
 #include <cstdint>
@@ -46,6 +47,20 @@ bool plan_grouped_retrieve(const Plan& p, const hkv_chunk_batch& b, GroupedCall*
 // Writes the grouped call's tables (out->ws layout, ws.total bytes) to `h`.
 void fill_grouped_tables(const Plan& p, const hkv_chunk_batch& b, const GroupedCall& g,
                          uint8_t* h);
+
+// A DMA retrieve: the live bytes of every page as copies, each run of pages
+// that are contiguous both in the object and in the pool merged into one.
+struct DmaRun {
+  uint64_t dst;    // pool address
+  uint64_t src;    // object address
+  uint64_t bytes;
+};
+
+// The runs of a retrieve of batch b into the pool at `pool` (in object order
+// per chunk and object group).  Null pages give nothing; a partial chunk's
+// MLA pages give their valid rows.
+void plan_dma_runs(const Plan& p, const hkv_chunk_batch& b, uint64_t pool,
+                   std::vector<DmaRun>* out);
 
 // Packs the call's block ids, object addresses and token counts into `t` and
 // sets a's inline offsets, if they fit in kInlineWords words; returns false

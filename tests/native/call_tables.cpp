@@ -6,7 +6,9 @@
 //     null-free batches;
 //   - the per-call tables packed into the kernel arguments read back as the
 //     batch's ids, object addresses and token counts, and are packed exactly
-//     when they fit.
+//     when they fit;
+//   - a DMA retrieve's runs move exactly the bytes of the plain launch's
+//     copies, each copy inside one run at the same offset on both sides.
 #include <cstdio>
 #include <cstring>
 #include <vector>
@@ -119,6 +121,30 @@ static int check(const char* name, std::vector<uint8_t> is_mla, int heads, int d
   if (b.chunk_tokens) memcpy(tab.data() + wl.tokens_off, toks.data(), n * 4);
   std::vector<Op> want, got;
   if (ops_of(name, p, tab.data(), tab.size(), wl.items_off, p.items.size(), wl.ids_off, wl.objs_off, wl.tokens_off, b.chunk_tokens != nullptr, n, obj_of, &want)) return 1;
+  if (!codec) {
+    // DMA retrieve: every plain copy lies inside one run at the same offset on
+    // both sides, and the runs move exactly the plain copies' bytes.
+    const uint64_t pool_base = 1ull << 44;
+    std::vector<hkv::DmaRun> runs;
+    hkv::plan_dma_runs(p, b, pool_base, &runs);
+    std::sort(runs.begin(), runs.end(), [](const hkv::DmaRun& x, const hkv::DmaRun& y) { return x.src < y.src; });
+    uint64_t run_bytes = 0, op_bytes = 0;
+    for (size_t i = 0; i < runs.size(); ++i) {
+      run_bytes += runs[i].bytes;
+      if (i && runs[i].src < runs[i - 1].src + runs[i - 1].bytes) FAIL("DMA runs overlap in the objects");
+    }
+    for (const Op& op : want) {
+      const uint64_t dst = pool_base + std::get<0>(op), len = std::get<1>(op);
+      const uint64_t src = (uint64_t)objp[std::get<2>(op) * O + std::get<3>(op)] + std::get<4>(op);
+      auto it = std::upper_bound(runs.begin(), runs.end(), src, [](uint64_t v, const hkv::DmaRun& r) { return v < r.src; });
+      if (it == runs.begin()) FAIL("a copy outside every DMA run");
+      --it;
+      if (src + len > it->src + it->bytes || dst - it->dst != src - it->src) FAIL("a copy not matched by its DMA run");
+      op_bytes += len;
+    }
+    if (run_bytes != op_bytes) FAIL("DMA runs move %llu bytes, the copies %llu", (unsigned long long)run_bytes, (unsigned long long)op_bytes);
+    printf("%-16s DMA: %zu runs for %zu copies (%llu bytes)\n", name, runs.size(), want.size(), (unsigned long long)run_bytes);
+  }
   hkv::GroupedCall g;
   const bool grouped = hkv::plan_grouped_retrieve(p, b, &g);
   if (grouped != expect_grouped) FAIL("grouped = %d, expected %d (%zu classes)", grouped, expect_grouped, g.members.size());

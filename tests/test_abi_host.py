@@ -210,6 +210,23 @@ def test_calls_past_the_item_limit_are_rejected_before_any_hip_call():
     assert "split" in hkv.hkv_last_error()
 
 
+def test_engine_choice_is_checked_before_any_hip_call():
+    """The DMA engine serves retrieves of byte-copied layouts only; other
+    engine values are rejected.  These checks precede any pointer use, so
+    fake addresses are safe here."""
+    plain = hkv.Layout(workloads.make_config("tiny").desc)
+    codec = hkv.Layout(dict(workloads.make_config("tiny").desc, kda_codec=1))
+    for lay, fn, engine in ((plain, hkv.hkv_store_chunks, hkv.HKV_ENGINE_DMA),
+                            (codec, hkv.hkv_retrieve_chunks, hkv.HKV_ENGINE_DMA),
+                            (plain, hkv.hkv_retrieve_chunks, 2),
+                            (plain, hkv.hkv_store_chunks, -1)):
+        ids = np.zeros((1, lay.G, lay.k), np.int32)
+        objs = [1 << 40] * lay.O
+        assert hkv.status_of(fn, lay.handle, 1 << 44, ids, objs, 1 << 45, 1 << 30, 0,
+                             lay.info, None, engine) == hkv.HKV_E_ARG
+        assert "engine" in hkv.hkv_last_error() or "DMA" in hkv.hkv_last_error()
+
+
 def test_one_hip_runtime_in_the_process():
     """libhkv must bind to the HIP runtime torch uses: two runtimes in one
     process each see the GPU alone (the second reports no device)."""

@@ -46,7 +46,14 @@ def _samples(rng, w, n_layers, k, count):
     return sorted(out)
 
 
-@pytest.mark.parametrize("name", W.CONFIG_NAMES + W.EXTRA_CONFIG_NAMES)
+# Duplex workloads run their phases at once; their parity test is
+# test_gpu_parity.py::test_host_duplex_parity (the sampled bookkeeping below
+# follows waves in order).
+FULL_SIZE = [n for n in W.CONFIG_NAMES + W.EXTRA_CONFIG_NAMES
+             if not W.make_config(n).extra.get("duplex")]
+
+
+@pytest.mark.parametrize("name", FULL_SIZE)
 def test_full_size_sampled(name):
     from workloads.runner import GpuWorkload
     cfg = W.make_config(name)

@@ -29,10 +29,13 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-def run_parity(cfg, tile_bytes=0, max_workgroups=0, pool_fill=None, objects="device"):
+def run_parity(cfg, tile_bytes=0, max_workgroups=0, pool_fill=None, objects="device",
+               retrieve_engine=None):
     from workloads.runner import GpuWorkload
-    _log(f"[parity] {cfg.name} tile={tile_bytes} max_wg={max_workgroups} objects={objects}")
-    g = GpuWorkload(cfg, tile_bytes=tile_bytes, max_workgroups=max_workgroups, objects=objects)
+    _log(f"[parity] {cfg.name} tile={tile_bytes} max_wg={max_workgroups} objects={objects} "
+         f"retrieve={retrieve_engine}")
+    g = GpuWorkload(cfg, tile_bytes=tile_bytes, max_workgroups=max_workgroups, objects=objects,
+                    retrieve_engine=retrieve_engine)
     ref = oracle.Layout(cfg.desc)
     for key, okey in (("num_blocks", "num_blocks"), ("pool_bytes_used", "pool_bytes_used"),
                       ("n_kv_groups", "n_kv_groups"), ("blocks_per_chunk", "blocks_per_chunk")):
@@ -505,3 +508,63 @@ def test_random_layouts(case):
     """Random small layouts, byte for byte against the oracle."""
     cfg, tile, max_wg = case
     run_parity(cfg, tile_bytes=tile, max_workgroups=max_wg)
+
+
+def test_host_duplex_parity():
+    """A store and a retrieve at the same time on two streams, objects in
+    pinned host memory (the host link carries both directions at once).  The
+    two touch different blocks and objects, so the result is the oracle's
+    retrieve and store applied one after the other."""
+    from workloads.runner import GpuWorkload
+    cfg = W.make_small_config("kl_tp1_host_duplex")
+    g = GpuWorkload(cfg, objects="host")
+    ref = oracle.Layout(cfg.desc)
+    used = ref.summary["pool_bytes_used"]
+    g.init_pool()
+    g.fill_objects(W.derive_seed(cfg.seed, 77))
+    g.synchronize()
+    torch.cuda.synchronize()
+    g.run_all()
+    torch.cuda.synchronize()
+    # the oracle: the same fills, then the waves in turn
+    ret = [w for w in g.waves if w.op == "retrieve"]
+    sto = [w for w in g.waves if w.op == "store"]
+    assert len(sto) == 1 and ret
+    seed = sto[0].pool_seed if sto[0].pool_seed is not None else W.initial_pool_seed(cfg)
+    pool_ref = W.fill_bytes(seed, 0, used)
+    objs_ref = {}
+    for rc in g.slot_of:
+        objs_ref[rc] = [W.fill_bytes(W.derive_seed(W.derive_seed(cfg.seed, 77), o),
+                                     g.slot_of[rc] * g.obj_stride[o], ref.obj_bytes(o))
+                        for o in range(ref.O)]
+    for w in ret:  # prefilled objects
+        for rc in w.chunks:
+            objs_ref[rc] = [W.fill_bytes(W.derive_seed(W.object_seed(cfg, *rc), o), 0,
+                                         ref.obj_bytes(o)) for o in range(ref.O)]
+    retrieved = {int(x) for w in ret for x in w.ids.ravel()} - {W.NULL_BLOCK}
+    stored = {int(x) for x in sto[0].ids.ravel()} - {W.NULL_BLOCK}
+    assert not retrieved & stored
+    for w in ret + sto:
+        (ref.store if w.op == "store" else ref.retrieve)(
+            pool_ref, w.ids, [objs_ref[rc] for rc in w.chunks], chunk_tokens=w.chunk_tokens)
+    assert np.array_equal(g.host_pool(), pool_ref)
+    for rc in g.slot_of:
+        for o in range(ref.O):
+            assert np.array_equal(g.host_object(rc, o), objs_ref[rc][o]), f"object {rc}/{o}"
+
+
+DMA_CASES = ([(W.make_small_config(n), "device") for n in
+              ("tiny", "kl_tp2", "k3_tp8", "long_ctx", "k3_tp8_holes", "kl_tp1_tails")] +
+             [(W.make_small_config("kl_tp1_host"), "host"), (W.make_config("tiny"), "host")] +
+             [(c, "device") for c in (EDGE[0], EDGE[1], EDGE[2], EDGE[3],
+                                      holes_and_tails(EDGE[2], 3, 33),
+                                      holes_and_tails(EDGE[1], 1, 0))] +
+             [(c, "device") for c, _, _ in random_layout_cases() if not c.desc["kda_codec"]][:20])
+
+
+@pytest.mark.parametrize("case", DMA_CASES, ids=lambda c: f"{c[0].name}-{c[1]}")
+def test_dma_retrieve_parity(case):
+    """Retrieves by DMA copies of contiguous page runs (objects in HBM or in
+    pinned host memory): the same bytes as the oracle, and as the kernels."""
+    cfg, objects = case
+    run_parity(cfg, objects=objects, retrieve_engine="dma")

@@ -292,6 +292,21 @@ def make_config(name: str) -> Config:
                        Phase("retrieve", _all_chunks(req), tail_tokens=tails)], seed,
                       notes="each request stores its whole first chunk and a partial second "
                             "chunk (160 MLA rows, no KDA snapshot: its block is not complete)")
+    if name == "kl_tp1_host_duplex":
+        seed = 0x48B000A
+        req = [8] * 16
+        desc = _desc(KIMI_LINEAR_27, 32, 128, 12288, 2, 1, 64 * GIB)
+        return Config(name, "Kimi-Linear full state (TP=1), path B, host objects: a store "
+                      "(kernels) and a retrieve (DMA) at the same time on two streams", desc, req,
+                      [Phase("retrieve", [(r, c) for r in range(8) for c in range(8)],
+                             prefilled_objects=True),
+                       Phase("store", [(r, c) for r in range(8, 16) for c in range(8)])],
+                      seed, shared_permutation=True,
+                      notes="requests 0-7 (64 chunks) are retrieved from pinned host objects "
+                            "while requests 8-15 (64 chunks) are stored to them, on two streams; "
+                            "the phases draw their block ids from one permutation, so they "
+                            "touch different blocks",
+                      extra={"objects": "host", "duplex": True, "retrieve_engine": "dma"})
     if name == "kl_tp1_int8":
         seed = 0x48B0009
         req = [8] * 128
@@ -308,7 +323,8 @@ def make_config(name: str) -> Config:
 
 CONFIG_NAMES = ("tiny", "kl_tp2", "kl_tp1", "k3_tp8", "long_ctx")
 # Further workloads beyond the five above.
-EXTRA_CONFIG_NAMES = ("kl_tp1_host", "k3_tp8_holes", "kl_tp1_tails", "kl_tp1_int8")
+EXTRA_CONFIG_NAMES = ("kl_tp1_host", "k3_tp8_holes", "kl_tp1_tails", "kl_tp1_int8",
+                      "kl_tp1_host_duplex")
 
 
 def make_small_config(name: str) -> Config:
@@ -338,6 +354,12 @@ def make_small_config(name: str) -> Config:
         cfg.requests = [4] * 5
         cfg.phases = [Phase("store", _all_chunks(cfg.requests)),
                       Phase("retrieve", _all_chunks(cfg.requests, first=2))]
+    elif name == "kl_tp1_host_duplex":
+        cfg.desc["pool_bytes"] = 1 * GIB
+        cfg.requests = [2] * 4
+        cfg.phases = [Phase("retrieve", [(r, c) for r in range(2) for c in range(2)],
+                            prefilled_objects=True),
+                      Phase("store", [(r, c) for r in range(2, 4) for c in range(2)])]
     elif name == "kl_tp1_host":
         cfg.desc["pool_bytes"] = 1 * GIB
         cfg.requests = [4] * 3

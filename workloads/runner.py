@@ -20,13 +20,18 @@ def _align(x: int, a: int = 256) -> int:
 class GpuWorkload:
     def __init__(self, cfg: W.Config, device: str = "cuda:0", tile_bytes: int = 0,
                  max_workgroups: int = 0, stream: torch.cuda.Stream | None = None,
-                 objects: str = "device"):
+                 objects: str = "device", retrieve_engine: str | None = None):
         """objects: "device" (HBM) or "host" (pinned host memory, which the
-        GPU reads and writes over the host link)."""
+        GPU reads and writes over the host link).  retrieve_engine: "kernel"
+        or "dma" (default: the workload's own choice, else "kernel")."""
         if objects not in ("device", "host"):
             raise ValueError("objects must be 'device' or 'host'")
         self.cfg = cfg
         self.objects_on = objects
+        engine = retrieve_engine or cfg.extra.get("retrieve_engine", "kernel")
+        if engine not in ("kernel", "dma"):
+            raise ValueError("retrieve_engine must be 'kernel' or 'dma'")
+        self.retrieve_engine = hkv.HKV_ENGINE_DMA if engine == "dma" else hkv.HKV_ENGINE_KERNEL
         self.device = torch.device(device)
         desc = dict(cfg.desc, tile_bytes=tile_bytes, max_workgroups=max_workgroups)
         self.layout = hkv.Layout(desc)
@@ -54,6 +59,12 @@ class GpuWorkload:
         max_chunks = max((len(w.chunks) for w in self.waves), default=0)
         self.ws_bytes = self.layout.workspace_size(max_chunks)
         self.ws = torch.empty(max(256, self.ws_bytes), dtype=torch.uint8, device=self.device)
+        # duplex workloads run their retrieves on a second stream, with a
+        # workspace of their own, beside the stores
+        self.duplex = bool(cfg.extra.get("duplex"))
+        self.stream2 = torch.cuda.Stream(device=self.device) if self.duplex else self.stream
+        self.ws2 = (torch.empty(max(256, self.ws_bytes), dtype=torch.uint8, device=self.device)
+                    if self.duplex else self.ws)
         self.pool_seed_of = {}   # (r, c) -> seed of the pool its store read
         self.store_ids = {}      # (r, c) -> [G][k] block ids its store read
 
@@ -106,17 +117,27 @@ class GpuWorkload:
                             v.numpy()[:] = W.fill_bytes(seed, 0, v.numel())
 
     # ------------------------------------------------------------ calls
+    def stream_of(self, w: W.Wave) -> torch.cuda.Stream:
+        """The stream a wave runs on: the second one for a duplex retrieve."""
+        return self.stream2 if (self.duplex and w.op == "retrieve") else self.stream
+
     def run_wave(self, w: W.Wave) -> None:
         ptrs = self.object_ptrs(w.chunks)
         fn = self.layout.store if w.op == "store" else self.layout.retrieve
-        fn(self.pool.data_ptr(), w.ids, ptrs, self.ws.data_ptr(), self.ws_bytes,
-           self.stream.cuda_stream, chunk_tokens=w.chunk_tokens)
+        second = self.duplex and w.op == "retrieve"
+        ws = self.ws2 if second else self.ws
+        engine = self.retrieve_engine if w.op == "retrieve" else hkv.HKV_ENGINE_KERNEL
+        fn(self.pool.data_ptr(), w.ids, ptrs, ws.data_ptr(), self.ws_bytes,
+           self.stream_of(w).cuda_stream, chunk_tokens=w.chunk_tokens, engine=engine)
 
     def run_all(self, on_wave=None) -> None:
         """Every wave in order.  A store wave with a pool seed first refills
         the pool with it.  Records, per stored chunk, the seed of the pool
         it read and its block ids."""
         self.prefill_objects()
+        if self.duplex:
+            self._run_all_duplex(on_wave)
+            return
         for i, w in enumerate(self.waves):
             if w.op == "store" and w.pool_seed is not None:
                 self.fill_pool(w.pool_seed)
@@ -129,6 +150,33 @@ class GpuWorkload:
             if on_wave is not None:
                 self.stream.synchronize()
                 on_wave(i, w)
+
+    def _run_all_duplex(self, on_wave) -> None:
+        """Duplex: one pool fill, then every wave at once (stores on the
+        first stream, retrieves on the second, which waits for the fills);
+        on_wave sees each wave after all have finished."""
+        seeds = [w.pool_seed for w in self.waves if w.op == "store" and w.pool_seed is not None]
+        if len(seeds) > 1:
+            raise ValueError("a duplex workload refills its pool once")
+        if seeds:
+            self.fill_pool(seeds[0])
+            self.current_pool_seed = seeds[0]
+        self.stream2.wait_stream(self.stream)
+        for w in self.waves:
+            if w.op == "store":
+                for n, rc in enumerate(w.chunks):
+                    self.pool_seed_of[rc] = self.current_pool_seed
+                    self.store_ids[rc] = w.ids[n].copy()
+            self.run_wave(w)
+        self.synchronize()
+        if on_wave is not None:
+            for i, w in enumerate(self.waves):
+                on_wave(i, w)
+
+    def synchronize(self) -> None:
+        self.stream.synchronize()
+        if self.duplex:
+            self.stream2.synchronize()
 
     current_pool_seed = None
 
