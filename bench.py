@@ -267,6 +267,10 @@ def main() -> int:
                          "(default: the workload's choice, else the kernel)")
     ap.add_argument("--max-workgroups", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step's calls into a HIP graph after the warm-up and "
+                         "time its replays (every call's tables must fit in its kernel "
+                         "arguments; one-stream workloads only)")
     ap.add_argument("--copy-ceiling", action="store_true",
                     help="also time torch copy_ of one 8 GiB buffer (a plain copy kernel of "
                          "known size, used to calibrate the rocprofv3 byte counters)")
@@ -337,21 +341,54 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
+    graph = None
+    if args.graph:
+        # the warm-up made each call's first, uncapturable, table upload
+        if g.duplex:
+            print("--graph: a duplex workload runs on two streams", file=sys.stderr)
+            return 2
+        import retrieve_store_chunk_amd as hkv
+        graph = torch.cuda.CUDAGraph()
+        try:
+            with torch.cuda.graph(graph, stream=stream):
+                one_step()
+        except hkv.HkvError as e:
+            print(f"--graph: {e}", file=sys.stderr)
+            return 2
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                graph.replay()
+        torch.cuda.synchronize()
+        log("step captured as one HIP graph")
+
+        def timed_step(events):
+            with torch.cuda.stream(stream):
+                events[0][0].record(stream)
+                graph.replay()
+                events[0][1].record(stream)
+    else:
+        timed_step = one_step
+
+    n_ev = 1 if graph is not None else n_w
     evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-            for _ in range(n_w)] for _ in range(args.steps)]
+            for _ in range(n_ev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        one_step(evs[s])
+        timed_step(evs[s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = step_payload / (ms_per_step / 1e3) / 1e9
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} GB/s")
 
-    # per-kernel: each call enqueues one tiny table upload and one launch
+    # per kernel (per graph replay with --graph), from the events around it
     kern = {}
-    for i, w in enumerate(g.waves):
+    if graph is not None:
+        kern["graph_replay"] = {"launches": args.steps, "hbm": step_hbm * args.steps,
+                                "link": sum(per_wave_link) * args.steps,
+                                "ms": sum(e[0][0].elapsed_time(e[0][1]) for e in evs)}
+    for i, w in enumerate(g.waves if graph is None else ()):
         name = ("hkv_store_gather" if w.op == "store" else
                 "retrieve_dma_copies" if g.retrieve_engine else "hkv_retrieve_scatter")
         ms = [evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]
@@ -417,7 +454,8 @@ def main() -> int:
                    "block_size": info["block_size"], "chunk_tokens": info["chunk_tokens"],
                    "path": "B packed" if info["path"] else "A padded-unified",
                    "tile_bytes": args.tile_bytes, "max_workgroups": args.max_workgroups,
-                   "retrieve_engine": "dma" if g.retrieve_engine else "kernel"},
+                   "retrieve_engine": "dma" if g.retrieve_engine else "kernel",
+                   "graph": graph is not None},
         "objects": objects_on,
         "pct_hbm_peak": None if on_host else
         round(100 * step_hbm / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 2),

@@ -51,6 +51,8 @@ typedef int32_t hkv_status;
 #define HKV_E_ALIGN (-8)     /* pool, object or workspace pointer not 16-byte aligned */
 #define HKV_E_WORKSPACE (-9) /* workspace NULL or smaller than hkv_workspace_size() */
 #define HKV_E_HIP (-10)      /* the HIP runtime reported an error (see hkv_last_error) */
+#define HKV_E_CAPTURE (-11)  /* the stream is capturing and the call cannot be captured
+                                (see hkv_store_chunks) */
 
 /* One rank's model shapes.  KDA state shapes are PER RANK: heads and conv_dim
  * are already divided by the TP degree, because the KDA state is sharded
@@ -268,10 +270,19 @@ hkv_status hkv_workspace_size(const hkv_layout* layout, int32_t max_chunks, size
  * same stream.
  * Repeated source ids are allowed.  Null ids and partial chunks: see
  * HKV_NULL_BLOCK and hkv_chunk_batch.chunk_tokens.
+ * Graph capture: while `stream` is capturing (hipStreamBeginCapture), a call
+ * whose tables travel in the kernel arguments is captured as its single
+ * launch, and a DMA retrieve as its copies; a replay moves the bytes the
+ * buffers hold at replay time.  Any other call returns HKV_E_CAPTURE and
+ * enqueues nothing: a larger call (its staged table copy would replay
+ * whatever the staging slot holds later), and a layout's first call on a
+ * device (it uploads the layout's tables synchronously).  Null ids and
+ * partial chunks are then served by one launch over all work items.
  * Errors: HKV_E_ARG (also a chunk_tokens entry outside [0, C]), HKV_E_RANGE
  * (an id neither HKV_NULL_BLOCK nor in [0, num_blocks)), HKV_E_ALIAS (objects
  * overlap each other, the pool or the workspace), HKV_E_ALIGN,
- * HKV_E_WORKSPACE, HKV_E_HIP (a HIP call failed; hkv_last_error names it). */
+ * HKV_E_WORKSPACE, HKV_E_CAPTURE, HKV_E_HIP (a HIP call failed;
+ * hkv_last_error names it). */
 hkv_status hkv_store_chunks(const hkv_layout* layout, const void* pool,
                             const hkv_chunk_batch* batch, void* workspace, size_t ws_bytes,
                             void* stream);
@@ -283,9 +294,10 @@ hkv_status hkv_store_chunks(const hkv_layout* layout, const void* pool,
  * writes only its valid MLA token rows).  Because all groups share one
  * block-id space, every non-null id of the call must be distinct
  * (HKV_E_ALIAS otherwise).
- * Same buffer rules as hkv_store_chunks; objects are not modified.
+ * Same buffer and capture rules as hkv_store_chunks; objects are not
+ * modified.
  * Errors: HKV_E_ARG, HKV_E_RANGE, HKV_E_ALIAS, HKV_E_ALIGN, HKV_E_WORKSPACE,
- * HKV_E_HIP. */
+ * HKV_E_CAPTURE, HKV_E_HIP. */
 hkv_status hkv_retrieve_chunks(const hkv_layout* layout, void* pool,
                                const hkv_chunk_batch* batch, void* workspace,
                                size_t ws_bytes, void* stream);

@@ -26,10 +26,12 @@ HKV_E_ALIAS = -7
 HKV_E_ALIGN = -8
 HKV_E_WORKSPACE = -9
 HKV_E_HIP = -10
+HKV_E_CAPTURE = -11
 
 STATUS_NAMES = {0: "HKV_OK", -1: "HKV_E_ARG", -2: "HKV_E_COVER", -3: "HKV_E_CHUNK",
                 -4: "HKV_E_BATCH", -5: "HKV_E_POOL", -6: "HKV_E_RANGE", -7: "HKV_E_ALIAS",
-                -8: "HKV_E_ALIGN", -9: "HKV_E_WORKSPACE", -10: "HKV_E_HIP"}
+                -8: "HKV_E_ALIGN", -9: "HKV_E_WORKSPACE", -10: "HKV_E_HIP",
+                -11: "HKV_E_CAPTURE"}
 
 i32, i64, u32, u64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_void_p
 

@@ -1,11 +1,12 @@
 // C ABI of the chunk store/retrieve library (declared in include/hkv.h).
 //
-// Per call: validate everything on the host, write the call's tables (layer
-// placements, work items, block ids, object addresses) into a pinned staging
-// slot, copy them into the caller's workspace on the caller's stream, and
-// launch one gather or scatter kernel on the same stream.  No call
-// synchronises the stream; a staging slot is reused only after the event
-// recorded behind its copy has completed.
+// Per call: validate everything on the host, then launch one gather or
+// scatter kernel on the caller's stream.  The call's own tables (block ids,
+// object addresses, token counts) go in the kernel arguments when they fit;
+// otherwise they are written into a pinned staging slot and copied into the
+// caller's workspace on the same stream first.  No call synchronises the
+// stream; a staging slot is reused only after the event recorded behind its
+// copy has completed.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -163,14 +164,17 @@ constexpr uint64_t layer_table_bytes(const hkv::Plan& p) {
 }
 
 // The layout's constant tables on `dev`: uploaded (synchronously) by the
-// first call there.
-hkv_status layout_tables(const hkv_layout* lay, int dev, const uint8_t** out) {
+// first call there, which therefore cannot be a captured one.
+hkv_status layout_tables(const hkv_layout* lay, int dev, bool capturing, const uint8_t** out) {
   std::lock_guard<std::mutex> g(lay->mu);
   auto it = lay->dev_tables.find(dev);
   if (it != lay->dev_tables.end()) {
     *out = static_cast<const uint8_t*>(it->second);
     return HKV_OK;
   }
+  if (capturing)
+    return set_error(HKV_E_CAPTURE, "the first call of a layout on a device uploads its tables "
+                                    "synchronously; make one call there before capturing");
   DeviceScope scope(dev);
   if (scope.err != hipSuccess) return hip_error(scope.err, "selecting the stream's device");
   const hkv::Plan& p = lay->plan;
@@ -335,6 +339,16 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   int dev = 0;
   st = stream_device(s, &dev);
   if (st != HKV_OK) return st;
+  // Under stream capture only what a graph can replay is enqueued: DMA
+  // copies between the caller's buffers, or one launch whose tables are in
+  // its arguments.  A copy out of a staging slot would replay whatever the
+  // ring later put in that slot.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (s) {
+    const hipError_t e = hipStreamIsCapturing(s, &cap);
+    if (e != hipSuccess) return hip_error(e, "querying the stream's capture status");
+  }
+  const bool capturing = cap != hipStreamCaptureStatusNone;
 
   if (b->engine == HKV_ENGINE_DMA) {
     // One copy per run of pages contiguous in both the object and the pool.
@@ -351,7 +365,7 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
     return HKV_OK;
   }
 
-  if (!store) {
+  if (!store && !capturing) {
     bool any_null = false;
     for (uint64_t i = 0; i < n_ids && !any_null; ++i) any_null = ids[i] == HKV_NULL_BLOCK;
     if (any_null || b->chunk_tokens) {
@@ -362,7 +376,7 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   }
 
   const uint8_t* tables = nullptr;
-  st = layout_tables(layout, dev, &tables);
+  st = layout_tables(layout, dev, capturing, &tables);
   if (st != HKV_OK) return st;
   const bool has_tokens = b->chunk_tokens != nullptr;
   hkv::CopyArgs a =
@@ -373,6 +387,9 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
     hkv::InlineTables t;
     if (hkv::pack_inline_tables(p, *b, &t, &a)) return launch_one(store, p, a, t, stream);
   }
+  if (capturing)
+    return set_error(HKV_E_CAPTURE, "the call's tables do not fit in the kernel arguments, "
+                                    "so it cannot be captured; split the batch");
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   const uint64_t lo = wl.ids_off;  // the per-call sections: ids, objects, tokens
   st = upload(dev, wsb + lo, wl.total - lo, s, [&](uint8_t* h) {

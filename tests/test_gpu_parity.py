@@ -568,3 +568,112 @@ def test_dma_retrieve_parity(case):
     pinned host memory): the same bytes as the oracle, and as the kernels."""
     cfg, objects = case
     run_parity(cfg, objects=objects, retrieve_engine="dma")
+
+
+# ------------------------------------------------------------ graph capture
+GRAPH_CASES = [("tiny", "kernel"), ("kl_tp1", "kernel"), ("kl_tp1", "dma"),
+               ("kl_tp1_tails", "kernel"), ("k3_tp8_holes", "kernel"),
+               ("kl_tp1_int8", "kernel")]
+
+
+def _first_calls(g, m):
+    """The first store and the first retrieve wave, cut to m chunks each:
+    (chunks, ids, chunk_tokens) per call."""
+    out = []
+    for op in ("store", "retrieve"):
+        w = next(w for w in g.waves if w.op == op)
+        tok = None if w.chunk_tokens is None else w.chunk_tokens[:m].copy()
+        out.append((w.chunks[:m], w.ids[:m].copy(), tok))
+    return out
+
+
+@pytest.mark.parametrize("name,engine", GRAPH_CASES, ids=lambda x: str(x))
+def test_graph_capture_replays_small_calls(name, engine):
+    """A store and a retrieve whose tables fit in the kernel arguments are
+    captured into one HIP graph.  The graph is replayed three times, with new
+    pool and object bytes written eagerly before each replay, and every
+    replay matches the oracle applied to that replay's inputs."""
+    import retrieve_store_chunk_amd as hkv
+    from workloads.runner import GpuWorkload
+    cfg = W.make_config(name) if name == "tiny" else W.make_small_config(name)
+    _log(f"[graph] {name} retrieve={engine}")
+    g = GpuWorkload(cfg, retrieve_engine=engine)
+    ref = oracle.Layout(cfg.desc)
+    (s_chunks, s_ids, s_tok), (r_chunks, r_ids, r_tok) = _first_calls(g, 8)
+    h, P, WS, wsb, S = g.layout.handle, g.pool.data_ptr(), g.ws.data_ptr(), g.ws_bytes, g.stream
+    eng = hkv.HKV_ENGINE_DMA if engine == "dma" else hkv.HKV_ENGINE_KERNEL
+    # the layout's first call on the device uploads its tables: not in a capture
+    g.init_pool()
+    hkv.hkv_store_chunks(h, P, s_ids, g.object_ptrs(s_chunks), WS, wsb, S.cuda_stream,
+                         chunk_tokens=s_tok)
+    S.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=S):
+        hkv.hkv_store_chunks(h, P, s_ids, g.object_ptrs(s_chunks), WS, wsb, S.cuda_stream,
+                             chunk_tokens=s_tok)
+        hkv.hkv_retrieve_chunks(h, P, r_ids, g.object_ptrs(r_chunks), WS, wsb, S.cuda_stream,
+                                chunk_tokens=r_tok, engine=eng)
+    used = ref.summary["pool_bytes_used"]
+    slots = list(dict.fromkeys(list(s_chunks) + list(r_chunks)))
+    for rep in range(3):
+        seed = W.derive_seed(cfg.seed, 7100 + rep)
+        pool_ref = W.fill_bytes(seed, 0, used)
+        g.pool[:used].copy_(torch.from_numpy(pool_ref))
+        objs_ref = {}
+        for i, rc in enumerate(slots):
+            objs_ref[rc] = [W.fill_bytes(W.derive_seed(seed, 1 + 4 * i + o), 0, ref.obj_bytes(o))
+                            for o in range(ref.O)]
+            for o in range(ref.O):
+                g.object_view(rc, o).copy_(torch.from_numpy(objs_ref[rc][o]))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref.store(pool_ref, s_ids, [objs_ref[rc] for rc in s_chunks], chunk_tokens=s_tok)
+        ref.retrieve(pool_ref, r_ids, [objs_ref[rc] for rc in r_chunks], chunk_tokens=r_tok)
+        assert np.array_equal(g.host_pool()[:used], pool_ref), f"pool differs on replay {rep}"
+        for rc in slots:
+            for o in range(ref.O):
+                assert np.array_equal(g.host_object(rc, o), objs_ref[rc][o]), \
+                    f"object {rc}/{o} differs on replay {rep}"
+
+
+def test_capture_refuses_calls_it_cannot_replay():
+    """Under capture, a layout's first call on the device and a call whose
+    tables need the workspace return HKV_E_CAPTURE and enqueue nothing."""
+    import retrieve_store_chunk_amd as hkv
+    from workloads.runner import GpuWorkload
+    cfg = call_size_config(129, False)
+    g = GpuWorkload(cfg)
+    g.init_pool()
+    g.fill_objects(3)
+    torch.cuda.synchronize()
+    w = next(w for w in g.waves if w.op == "store")
+    assert len(w.chunks) == 129
+    h, P, WS, wsb, S = g.layout.handle, g.pool.data_ptr(), g.ws.data_ptr(), g.ws_bytes, g.stream
+    ptrs = g.object_ptrs(w.chunks)
+    pool0 = g.host_pool().copy()
+    objs0 = [g.host_object(rc, o) for rc in w.chunks for o in range(g.layout.O)]
+    x = torch.zeros(16, device=g.device)
+    first = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(first, stream=S):
+        x.add_(1)
+        st_first = hkv.status_of(hkv.hkv_store_chunks, h, P, w.ids[:1], ptrs[:g.layout.O], WS,
+                                 wsb, S.cuda_stream)
+    assert st_first == hkv.HKV_E_CAPTURE
+    hkv.hkv_store_chunks(h, P, w.ids[:1], ptrs[:g.layout.O], WS, wsb, S.cuda_stream)
+    S.synchronize()
+    objs0[:g.layout.O] = [g.host_object(w.chunks[0], o) for o in range(g.layout.O)]
+    large = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(large, stream=S):
+        x.add_(1)
+        st_store = hkv.status_of(hkv.hkv_store_chunks, h, P, w.ids, ptrs, WS, wsb, S.cuda_stream)
+        st_retrieve = hkv.status_of(hkv.hkv_retrieve_chunks, h, P, w.ids, ptrs, WS, wsb,
+                                    S.cuda_stream)
+    assert st_store == st_retrieve == hkv.HKV_E_CAPTURE
+    first.replay()
+    large.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(x.cpu(), torch.full((16,), 2.0))
+    assert np.array_equal(g.host_pool(), pool0)
+    got = [g.host_object(rc, o) for rc in w.chunks for o in range(g.layout.O)]
+    assert all(np.array_equal(a, b) for a, b in zip(got, objs0))
