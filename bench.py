@@ -388,9 +388,11 @@ def main() -> int:
         kern["graph_replay"] = {"launches": args.steps, "hbm": step_hbm * args.steps,
                                 "link": sum(per_wave_link) * args.steps,
                                 "ms": sum(e[0][0].elapsed_time(e[0][1]) for e in evs)}
+    # INT8 layouts run the kernel pair built for their KDA head_dim
+    sfx = f"_int8_d{cfg.desc['kda_head_dim']}" if info.get("kda_codec") else ""
     for i, w in enumerate(g.waves if graph is None else ()):
-        name = ("hkv_store_gather" if w.op == "store" else
-                "retrieve_dma_copies" if g.retrieve_engine else "hkv_retrieve_scatter")
+        name = ("hkv_store_gather" + sfx if w.op == "store" else
+                "retrieve_dma_copies" if g.retrieve_engine else "hkv_retrieve_scatter" + sfx)
         ms = [evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]
         k = kern.setdefault(name, {"launches": 0, "ms": 0.0, "hbm": 0, "link": 0})
         k["launches"] += args.steps
@@ -429,7 +431,7 @@ def main() -> int:
     else:
         achieved = kernels[dom]["hbm_GBs"]
         traffic = load_traffic(args.config, args.tile_bytes, args.max_workgroups) \
-            if dom == "hkv_store_gather" else None
+            if dom.startswith("hkv_store_gather") else None
         roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic}

@@ -209,6 +209,7 @@ hkv::CopyArgs base_args(const hkv::Plan& p, const void* pool, const uint8_t* lay
   a.block_tokens = (uint64_t)p.block_size;
   a.tile_bytes = p.tile_bytes;
   a.codec_rows_per_item = p.codec_rows_per_item;
+  a.codec_head_dim = p.kda_codec ? (uint32_t)p.shapes[1] : 0u;  // kda_head_dim
   a.items_per_chunk = (uint32_t)n_items;
   a.n_kv_groups = (uint32_t)p.n_kv_groups;
   a.blocks_per_chunk = (uint32_t)p.blocks_per_chunk;
@@ -229,8 +230,8 @@ hkv_status launch_one(bool store, const hkv::Plan& p, const hkv::CopyArgs& a,
   if (grid > grid_limit) grid = grid_limit;
   const int e = hkv::launch_copy(store, a, t, (uint32_t)grid, stream);
   if (e != 0)
-    return hip_error((hipError_t)e, store ? "launching hkv_store_gather"
-                                          : "launching hkv_retrieve_scatter");
+    return hip_error((hipError_t)e, store ? "launching the gather kernel"
+                                          : "launching the scatter kernel");
   return HKV_OK;
 }
 

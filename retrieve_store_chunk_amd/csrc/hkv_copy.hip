@@ -23,7 +23,13 @@
 //     the Kimi-Linear TP=1 shapes, against 6.1 and 5.2 TB/s with 256 KiB
 //     tiles and no remap);
 //   - only real page bytes are touched, so KDA padding (path A) and group
-//     slack (path B) are never read or written.
+//     slack (path B) are never read or written;
+//   - layouts without the INT8 codec run a kernel pair with no codec code;
+//     INT8 layouts run the pair built for their head_dim, so that each
+//     kernel holds only the registers its own path needs.  The plain gather
+//     is capped at 6 waves per SIMD (an LDS reservation at launch), where it
+//     measured best; the INT8 gather runs best at 8, which its registers
+//     allow.
 // A page is opaque bytes ("Kimi-Linear" recipe: the KDA state is an opaque
 // page), so data only ever lives in integer vector registers: NaN payloads
 // of bf16/fp8 values pass unchanged.
@@ -61,6 +67,9 @@ namespace {
 #endif
 #ifndef HKV_CODEC_NT
 #define HKV_CODEC_NT 1    // nontemporal code / scale accesses in the codec
+#endif
+#ifndef HKV_GATHER_LDS
+#define HKV_GATHER_LDS 13312  // LDS bytes reserved per workgroup of the plain gather (occupancy cap)
 #endif
 #ifndef HKV_WAVES_PER_EU
 #define HKV_WAVES_PER_EU 0  // waves per SIMD the register budget must allow (0: any)
@@ -262,21 +271,12 @@ __device__ __forceinline__ void codec_rows(const hkv::CopyArgs& a,
 }
 
 // The codec for the layer's head_dim (the planner admits 16..256, powers of two).
-template <bool kStore>
-__device__ __forceinline__ void codec_dispatch(const hkv::CopyArgs& a,
-                                               const HKV_CONST hkv::DevLayer* L, int32_t id,
-                                               uint8_t* obj_page, uint32_t group) {
-  switch (L->head_dim) {
-    case 16: codec_rows<16, kStore>(a, L, id, obj_page, group); break;
-    case 32: codec_rows<32, kStore>(a, L, id, obj_page, group); break;
-    case 64: codec_rows<64, kStore>(a, L, id, obj_page, group); break;
-    case 128: codec_rows<128, kStore>(a, L, id, obj_page, group); break;
-    case 256: codec_rows<256, kStore>(a, L, id, obj_page, group); break;
-    default: break;
-  }
-}
 
-template <bool kStore, uint32_t kUnroll, uint32_t kRun>
+// kD: 0 for a layout without the codec; else the KDA head_dim of an INT8
+// layout, whose kind-1 items quantise or dequantise rows of kD values.  One
+// kernel per head_dim keeps each kernel's registers to what its own codec
+// path needs (more waves in flight than a kernel holding every head_dim).
+template <bool kStore, uint32_t kUnroll, uint32_t kRun, uint32_t kD>
 __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a, const hkv::InlineTables& t) {
   const HKV_CONST hkv::DevLayer* layers = (const HKV_CONST hkv::DevLayer*)a.layers;
   const HKV_CONST uint64_t* items = (const HKV_CONST uint64_t*)a.items;
@@ -308,8 +308,8 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a, const hkv::In
     const int32_t id = ids[((uint64_t)c * a.n_kv_groups + L->kv_group) * a.blocks_per_chunk + j];
     uint8_t* obj = reinterpret_cast<uint8_t*>(objs[(uint64_t)c * a.n_obj_groups + L->obj_group]);
     uint8_t* obj_page = obj + L->obj_offset + (uint64_t)j * L->obj_page;
-    if (w >> 63) {  // a codec row group of a KDA page
-      codec_dispatch<kStore>(a, L, id, obj_page, s);
+    if (w >> 63) {  // a codec row group of a KDA page (INT8 layouts only)
+      if constexpr (kD != 0) codec_rows<kD, kStore>(a, L, id, obj_page, s);
       continue;
     }
     const uint64_t span = L->copy_bytes;  // the page, or the conv part under the codec
@@ -340,26 +340,61 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a, const hkv::In
 
 }  // namespace
 
-extern "C" __global__ __launch_bounds__(kThreads) HKV_OCCUPANCY
-void hkv_store_gather(hkv::CopyArgs a, hkv::InlineTables t) {
-  copy_items<true, HKV_STORE_UNROLL, HKV_STORE_XCD_RUN>(a, t);
-}
+// The gather (store) and scatter (retrieve) kernels: one pair for layouts
+// without the codec, and one pair per head_dim for INT8 layouts.
+#define HKV_KERNEL_PAIR(suffix, kD)                                            \
+  extern "C" __global__ __launch_bounds__(kThreads) HKV_OCCUPANCY void         \
+      hkv_store_gather##suffix(hkv::CopyArgs a, hkv::InlineTables t) {         \
+    copy_items<true, HKV_STORE_UNROLL, HKV_STORE_XCD_RUN, kD>(a, t);           \
+  }                                                                            \
+  extern "C" __global__ __launch_bounds__(kThreads) HKV_OCCUPANCY void         \
+      hkv_retrieve_scatter##suffix(hkv::CopyArgs a, hkv::InlineTables t) {     \
+    copy_items<false, HKV_RETRIEVE_UNROLL, HKV_RETRIEVE_XCD_RUN, kD>(a, t);    \
+  }
 
-extern "C" __global__ __launch_bounds__(kThreads) HKV_OCCUPANCY
-void hkv_retrieve_scatter(hkv::CopyArgs a, hkv::InlineTables t) {
-  copy_items<false, HKV_RETRIEVE_UNROLL, HKV_RETRIEVE_XCD_RUN>(a, t);
-}
+HKV_KERNEL_PAIR(, 0)
+HKV_KERNEL_PAIR(_int8_d16, 16)
+HKV_KERNEL_PAIR(_int8_d32, 32)
+HKV_KERNEL_PAIR(_int8_d64, 64)
+HKV_KERNEL_PAIR(_int8_d128, 128)
+HKV_KERNEL_PAIR(_int8_d256, 256)
+#undef HKV_KERNEL_PAIR
 
 namespace hkv {
 
 int launch_copy(bool store, const CopyArgs& a, const InlineTables& t, uint32_t grid,
                 void* stream) {
   if (grid == 0) return 0;
+  struct Pair {
+    uint32_t head_dim;
+    const void* store;
+    const void* retrieve;
+  };
+  static const Pair kPairs[] = {
+      {0, reinterpret_cast<const void*>(&hkv_store_gather),
+       reinterpret_cast<const void*>(&hkv_retrieve_scatter)},
+      {16, reinterpret_cast<const void*>(&hkv_store_gather_int8_d16),
+       reinterpret_cast<const void*>(&hkv_retrieve_scatter_int8_d16)},
+      {32, reinterpret_cast<const void*>(&hkv_store_gather_int8_d32),
+       reinterpret_cast<const void*>(&hkv_retrieve_scatter_int8_d32)},
+      {64, reinterpret_cast<const void*>(&hkv_store_gather_int8_d64),
+       reinterpret_cast<const void*>(&hkv_retrieve_scatter_int8_d64)},
+      {128, reinterpret_cast<const void*>(&hkv_store_gather_int8_d128),
+       reinterpret_cast<const void*>(&hkv_retrieve_scatter_int8_d128)},
+      {256, reinterpret_cast<const void*>(&hkv_store_gather_int8_d256),
+       reinterpret_cast<const void*>(&hkv_retrieve_scatter_int8_d256)},
+  };
+  const void* fn = nullptr;
+  for (const Pair& k : kPairs)
+    if (k.head_dim == a.codec_head_dim) fn = store ? k.store : k.retrieve;
+  if (!fn) return (int)hipErrorInvalidValue;  // the planner admits no other head_dim
   CopyArgs arg = a;
   void* params[] = {&arg, const_cast<InlineTables*>(&t)};
-  const void* fn = store ? reinterpret_cast<const void*>(&hkv_store_gather)
-                         : reinterpret_cast<const void*>(&hkv_retrieve_scatter);
-  return (int)hipLaunchKernel(fn, dim3(grid), dim3(kThreads), params, 0,
+  // The plain gather needs few registers and would run 8 waves per SIMD; it
+  // measured best at 6.  Reserving LDS it does not use caps a CU at 12
+  // workgroups (160 KiB / 13 KiB).
+  const uint32_t lds = (store && a.codec_head_dim == 0) ? HKV_GATHER_LDS : 0u;
+  return (int)hipLaunchKernel(fn, dim3(grid), dim3(kThreads), params, lds,
                               reinterpret_cast<hipStream_t>(stream));
 }
 

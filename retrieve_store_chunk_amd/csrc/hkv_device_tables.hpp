@@ -88,6 +88,7 @@ struct CopyArgs {
   uint64_t block_tokens;   // N
   uint64_t tile_bytes;
   uint32_t codec_rows_per_item;  // rows quantized by one kind-1 item (whole passes)
+  uint32_t codec_head_dim;  // INT8 layouts: the KDA head_dim (selects the kernels); else 0
   uint32_t items_per_chunk;
   uint32_t n_kv_groups;
   uint32_t blocks_per_chunk;
