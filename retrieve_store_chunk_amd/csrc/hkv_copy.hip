@@ -26,10 +26,10 @@
 //     slack (path B) are never read or written;
 //   - layouts without the INT8 codec run a kernel pair with no codec code;
 //     INT8 layouts run the pair built for their head_dim, so that each
-//     kernel holds only the registers its own path needs.  The plain gather
-//     is capped at 6 waves per SIMD (an LDS reservation at launch), where it
-//     measured best; the INT8 gather runs best at 8, which its registers
-//     allow.
+//     kernel holds only the registers its own path needs.  The plain
+//     kernels are capped by an LDS reservation at launch at 12 (gather) and
+//     13 (scatter) workgroups per CU, where they measured best; the INT8
+//     gather runs best at 8 waves per SIMD, which its registers allow.
 // A page is opaque bytes ("Kimi-Linear" recipe: the KDA state is an opaque
 // page), so data only ever lives in integer vector registers: NaN payloads
 // of bf16/fp8 values pass unchanged.
@@ -70,6 +70,9 @@ namespace {
 #endif
 #ifndef HKV_GATHER_LDS
 #define HKV_GATHER_LDS 13312  // LDS bytes reserved per workgroup of the plain gather (occupancy cap)
+#endif
+#ifndef HKV_SCATTER_LDS
+#define HKV_SCATTER_LDS 12288  // the same for the plain scatter
 #endif
 #ifndef HKV_WAVES_PER_EU
 #define HKV_WAVES_PER_EU 0  // waves per SIMD the register budget must allow (0: any)
@@ -390,10 +393,10 @@ int launch_copy(bool store, const CopyArgs& a, const InlineTables& t, uint32_t g
   if (!fn) return (int)hipErrorInvalidValue;  // the planner admits no other head_dim
   CopyArgs arg = a;
   void* params[] = {&arg, const_cast<InlineTables*>(&t)};
-  // The plain gather needs few registers and would run 8 waves per SIMD; it
-  // measured best at 6.  Reserving LDS it does not use caps a CU at 12
-  // workgroups (160 KiB / 13 KiB).
-  const uint32_t lds = (store && a.codec_head_dim == 0) ? HKV_GATHER_LDS : 0u;
+  // The plain kernels need few registers and would run 8 waves per SIMD; they
+  // measured best with fewer.  Reserving LDS they do not use caps a CU at 12
+  // gather workgroups (160 KiB / 13 KiB) or 13 scatter workgroups (12 KiB).
+  const uint32_t lds = a.codec_head_dim != 0 ? 0u : store ? HKV_GATHER_LDS : HKV_SCATTER_LDS;
   return (int)hipLaunchKernel(fn, dim3(grid), dim3(kThreads), params, lds,
                               reinterpret_cast<hipStream_t>(stream));
 }
