@@ -37,6 +37,25 @@ def test_library_exports_every_declared_function():
         assert hasattr(hkv.lib, n), n
 
 
+def test_every_codec_head_dim_has_its_kernel_pair():
+    """The launcher runs an INT8 layout on the kernel pair built for its KDA
+    head_dim, so every head_dim the planner admits under the codec needs
+    both kernels in the library."""
+    admitted = []
+    for d in range(1, 1025):
+        desc = workloads._desc([0, 1], 1, d, 8, 2, 1, 1 << 26, kda_codec=1)
+        try:
+            hkv.hkv_layout_destroy(hkv.hkv_layout_init(desc))
+            admitted.append(d)
+        except hkv.HkvError as e:
+            assert e.status == hkv.HKV_E_ARG
+    assert admitted == [16, 32, 64, 128, 256]
+    for d in admitted:
+        for kernel in ("hkv_store_gather_int8_d", "hkv_retrieve_scatter_int8_d"):
+            assert hasattr(hkv.lib, f"{kernel}{d}"), f"{kernel}{d}"
+    assert hasattr(hkv.lib, "hkv_store_gather") and hasattr(hkv.lib, "hkv_retrieve_scatter")
+
+
 def same_plan(desc):
     ref = oracle.Layout(desc)
     got = hkv.Layout(desc)
