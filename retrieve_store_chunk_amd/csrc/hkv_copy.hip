@@ -57,7 +57,7 @@ namespace {
 #define HKV_NT_STORE 1    // nontemporal stores
 #endif
 #ifndef HKV_XCD_REMAP
-#define HKV_XCD_REMAP 1   // give each XCD a contiguous range of work items
+#define HKV_XCD_REMAP 1   // remap item order per XCD (hkv::xcd_first_item)
 #endif
 #ifndef HKV_STORE_XCD_RUN
 #define HKV_STORE_XCD_RUN 0        // gather: >0 = XCDs take turns on runs of this many items
@@ -273,12 +273,11 @@ __device__ __forceinline__ void codec_rows(const hkv::CopyArgs& a,
   }
 }
 
-// The codec for the layer's head_dim (the planner admits 16..256, powers of two).
-
-// kD: 0 for a layout without the codec; else the KDA head_dim of an INT8
-// layout, whose kind-1 items quantise or dequantise rows of kD values.  One
-// kernel per head_dim keeps each kernel's registers to what its own codec
-// path needs (more waves in flight than a kernel holding every head_dim).
+// The work items of a call.  kD: 0 for a layout without the codec; else the
+// KDA head_dim of an INT8 layout (16..256, powers of two), whose kind-1 items
+// quantise or dequantise rows of kD values.  One kernel per head_dim keeps
+// each kernel's registers to what its own codec path needs (more waves in
+// flight than a kernel holding every head_dim).
 template <bool kStore, uint32_t kUnroll, uint32_t kRun, uint32_t kD>
 __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a, const hkv::InlineTables& t) {
   const HKV_CONST hkv::DevLayer* layers = (const HKV_CONST hkv::DevLayer*)a.layers;
