@@ -260,7 +260,8 @@ def main() -> int:
                     help="workload: tiny, kl_tp2, kl_tp1 (default), k3_tp8, long_ctx, "
                          "kl_tp1_host (objects in pinned host memory), k3_tp8_holes, "
                          "kl_tp1_tails, kl_tp1_int8 (INT8 KDA objects), kl_tp1_host_duplex "
-                         "(host objects, a store and a retrieve at once on two streams)")
+                         "(host objects, a store and a retrieve at once on two streams), "
+                         "kl_tp1_int8_host (INT8 KDA objects in pinned host memory)")
     ap.add_argument("--tile-bytes", type=int, default=0)
     ap.add_argument("--retrieve-engine", choices=("kernel", "dma"), default=None,
                     help="retrieves by the scatter kernel or by DMA copies of page runs "

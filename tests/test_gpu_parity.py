@@ -414,7 +414,9 @@ def test_codec_with_holes_and_tails(cfg):
 
 
 def test_codec_host_objects():
-    run_parity(W.make_small_config("kl_tp1_int8"), objects="host")
+    cfg = W.make_small_config("kl_tp1_int8_host")
+    assert cfg.extra["objects"] == "host" and cfg.desc["kda_codec"] == 1
+    run_parity(cfg, objects="host")
 
 
 @pytest.mark.parametrize("cfg", [varied_tails(mini_config("varied", [0, 1, 0, 1], 1, chunk_min=40,

@@ -318,13 +318,25 @@ def make_config(name: str) -> Config:
                       notes="the Kimi-Linear TP=1 workload with the INT8 codec of KDA "
                             "checkpoints: 3.5x smaller KDA objects, quantised on store and "
                             "dequantised on retrieve in the same pass")
+    if name == "kl_tp1_int8_host":
+        seed = 0x48B000B
+        req = [8] * 16
+        desc = _desc(KIMI_LINEAR_27, 32, 128, 12288, 2, 1, 64 * GIB, kda_codec=1)
+        return Config(name, "Kimi-Linear full state (TP=1), path B, INT8 KDA objects in "
+                      "pinned host memory", desc, req,
+                      [Phase("store", _all_chunks(req)),
+                       Phase("retrieve", _all_chunks(req, first=4))], seed,
+                      notes="the host-object workload with the INT8 codec: 16 requests x 8 "
+                            "chunks stored to host objects (2.2 GB pinned instead of 7.5 GB), "
+                            "the first 4 chunks of each retrieved from them",
+                      extra={"objects": "host"})
     raise KeyError(name)
 
 
 CONFIG_NAMES = ("tiny", "kl_tp2", "kl_tp1", "k3_tp8", "long_ctx")
 # Further workloads beyond the five above.
 EXTRA_CONFIG_NAMES = ("kl_tp1_host", "k3_tp8_holes", "kl_tp1_tails", "kl_tp1_int8",
-                      "kl_tp1_host_duplex")
+                      "kl_tp1_host_duplex", "kl_tp1_int8_host")
 
 
 def make_small_config(name: str) -> Config:
@@ -360,7 +372,7 @@ def make_small_config(name: str) -> Config:
         cfg.phases = [Phase("retrieve", [(r, c) for r in range(2) for c in range(2)],
                             prefilled_objects=True),
                       Phase("store", [(r, c) for r in range(2, 4) for c in range(2)])]
-    elif name == "kl_tp1_host":
+    elif name in ("kl_tp1_host", "kl_tp1_int8_host"):
         cfg.desc["pool_bytes"] = 1 * GIB
         cfg.requests = [4] * 3
         cfg.phases = [Phase("store", _all_chunks(cfg.requests)),
