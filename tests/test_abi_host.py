@@ -258,3 +258,50 @@ def test_one_hip_runtime_in_the_process():
     hsa = set(re.findall(r"\S*libhsa-runtime64\S*", maps))
     assert len(hip) == 1, hip
     assert len(hsa) == 1, hsa
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake device addresses: host-only check")
+def test_error_messages_are_per_thread():
+    """hkv_last_error is per calling thread: eight threads failing at the same
+    time for different reasons (the calls drop the interpreter lock) each
+    read back their own message every time."""
+    import threading
+    lay = hkv.Layout(workloads.make_config("tiny").desc)
+    G, k, O = lay.G, lay.k, lay.O
+    nb = lay.info["num_blocks"]
+    pool = 1 << 40
+    objs = [pool + (1 << 30) + i * (1 << 20) for i in range(2 * O)]
+    ws_bytes = lay.workspace_size(2)
+    ws = pool + (1 << 32)
+    ids = np.arange(2 * G * k, dtype=np.int32).reshape(2, G, k)
+    bad = ids.copy()
+    bad[1, 0, 0] = nb
+    cases = [(dict(ids=bad), hkv.HKV_E_RANGE, f"block id {nb} outside"),
+             (dict(pool=pool + 8), hkv.HKV_E_ALIGN, "pool pointer is not 16-byte aligned"),
+             (dict(ws_bytes=16), hkv.HKV_E_WORKSPACE, "workspace needs"),
+             (dict(objs=[objs[0]] * len(objs)), hkv.HKV_E_ALIAS, "overlaps")]
+    start = threading.Barrier(8)
+    failures = []
+
+    def worker(i):
+        kw, want, text = cases[i % len(cases)]
+        a = dict(pool=pool, ids=ids, objs=objs, ws=ws, ws_bytes=ws_bytes)
+        a.update(kw)
+        fn = hkv.hkv_store_chunks if i % 2 else hkv.hkv_retrieve_chunks
+        start.wait()
+        for _ in range(2000):
+            try:
+                fn(lay.handle, a["pool"], a["ids"], a["objs"], a["ws"], a["ws_bytes"], 0)
+                failures.append((i, "no error"))
+                return
+            except hkv.HkvError as e:
+                if e.status != want or text not in str(e):
+                    failures.append((i, str(e)))
+                    return
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not failures, failures[:4]

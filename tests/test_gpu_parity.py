@@ -679,3 +679,74 @@ def test_capture_refuses_calls_it_cannot_replay():
     assert np.array_equal(g.host_pool(), pool0)
     got = [g.host_object(rc, o) for rc in w.chunks for o in range(g.layout.O)]
     assert all(np.array_equal(a, b) for a, b in zip(got, objs0))
+
+
+# ------------------------------------------------------------ threads
+def test_calls_from_several_threads_at_once():
+    """Four host threads call store, then retrieve, at the same moment on one
+    shared layout, each on its own stream with its own workspace.  The first
+    calls are the layout's first on the device (its table upload), and every
+    batch is too large for the kernel arguments (its tables go through the
+    shared staging ring).  Retrieve targets are disjoint across threads.
+    Every object and the whole pool match the oracle."""
+    import threading
+    import retrieve_store_chunk_amd as hkv
+    desc = W._desc([0, 0, 1, 0, 1], 1, 16, 8, 2, 1, 1 << 28, mla_width=576)
+    lay, ref = hkv.Layout(desc), oracle.Layout(desc)
+    G, k, O = lay.G, lay.k, lay.O
+    nb, used = lay.info["num_blocks"], lay.info["pool_bytes_used"]
+    n_threads, n = 4, 200
+    assert (n * G * k + 1) // 2 + n * O > 384  # past the kernel-argument tables
+    assert n_threads * n * G * k <= nb
+    _log(f"[threads] {n_threads} x {n} chunks, G={G} k={k} O={O} blocks={nb}")
+    dev = torch.device("cuda")
+    pool_ref = W.fill_bytes(0x7EAD, 0, used)
+    pool = torch.from_numpy(pool_ref.copy()).to(dev)
+    rng = np.random.default_rng(0x7EAD)
+    stride = [max(256, (lay.info["obj_bytes"][o] + 255) // 256 * 256) for o in range(O)]
+    objs = [[torch.empty(n * stride[o], dtype=torch.uint8, device=dev) for o in range(O)]
+            for _ in range(n_threads)]
+    ptrs = [[objs[t][o].data_ptr() + c * stride[o] for c in range(n) for o in range(O)]
+            for t in range(n_threads)]
+    store_ids = [rng.integers(0, nb, (n, G, k)).astype(np.int32) for _ in range(n_threads)]
+    perm = rng.permutation(nb)[: n_threads * n * G * k].astype(np.int32)
+    retr_ids = [perm[t * n * G * k:(t + 1) * n * G * k].reshape(n, G, k).copy()
+                for t in range(n_threads)]
+    wsb = lay.workspace_size(n)
+    ws = [torch.empty(wsb, dtype=torch.uint8, device=dev) for _ in range(n_threads)]
+    streams = [torch.cuda.Stream(device=dev) for _ in range(n_threads)]
+    torch.cuda.synchronize()
+    start = threading.Barrier(n_threads)
+    errors = []
+
+    def worker(t, op):
+        try:
+            start.wait()
+            fn, ids = (lay.store, store_ids[t]) if op == "store" else (lay.retrieve, retr_ids[t])
+            fn(pool.data_ptr(), ids, ptrs[t], ws[t].data_ptr(), wsb, streams[t].cuda_stream)
+            streams[t].synchronize()
+        except Exception as e:  # reported after the join
+            errors.append((t, op, repr(e)))
+
+    for op in ("store", "retrieve"):
+        threads = [threading.Thread(target=worker, args=(t, op)) for t in range(n_threads)]
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join()
+        assert not errors, errors
+    torch.cuda.synchronize()
+    # the oracle, one thread after another (stores read the pool before any
+    # retrieve writes it; retrieve targets are disjoint)
+    objs_ref = [[[np.zeros(ref.obj_bytes(o), np.uint8) for o in range(O)] for _ in range(n)]
+                for _ in range(n_threads)]
+    for t in range(n_threads):
+        ref.store(pool_ref, store_ids[t], objs_ref[t])
+    for t in range(n_threads):
+        ref.retrieve(pool_ref, retr_ids[t], objs_ref[t])
+    for t in range(n_threads):
+        for o in range(O):
+            got = objs[t][o].cpu().numpy().reshape(n, stride[o])[:, :ref.obj_bytes(o)]
+            want = np.stack([objs_ref[t][c][o] for c in range(n)])
+            assert np.array_equal(got, want), f"thread {t} objects {o}"
+    assert np.array_equal(pool[:used].cpu().numpy(), pool_ref), "pool"
