@@ -1,6 +1,4 @@
-"""Not collected until it has run on a GPU (pytest tests/wip_gpu_c_example.py).
-
-The C-ABI example (examples/roundtrip.cpp): a store and a retrieve through
+"""The C-ABI example (examples/roundtrip.cpp): a store and a retrieve through
 include/hkv.h and the HIP runtime alone, run as a process of its own.  Every
 stored page must come back byte for byte at its fresh block id and nothing
 else in the second pool may change."""
