@@ -48,3 +48,20 @@ def test_wave_bytes_match_page_by_page_count(name, codec):
         assert got == brute(ref, w)
         if not codec:
             assert got[0] == got[2]
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), (["--gpus", "8", "--steps", "1"], {}),
+                                      ([], {"WORLD_SIZE": "2"})])
+def test_bench_refuses_more_than_one_gpu(argv, env):
+    """The path has no cross-GPU step: bench.py runs on one GPU and says so
+    (exit 2, before it touches torch or a device)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *argv],
+                       capture_output=True, text=True, timeout=120, cwd=root,
+                       env=dict(os.environ, **env))
+    assert r.returncode == 2, r.stdout + r.stderr
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
