@@ -251,7 +251,7 @@ def chunk_keys_timing(g, cfg, tokens_per_request: int = 16384) -> dict:
             "what": "host, one thread, one call per request (hash blocks of N tokens)"}
 
 
-def main() -> int:
+def build_parser() -> argparse.ArgumentParser:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -281,7 +281,11 @@ def main() -> int:
     ap.add_argument("--hbm-ceiling", action="store_true",
                     help="also time pure-read, pure-write and contiguous-copy kernels built "
                          "like the library's (HBM reference rates)")
-    args = ap.parse_args()
+    return ap
+
+
+def main() -> int:
+    args = build_parser().parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the store/retrieve path has no cross-GPU "
