@@ -124,6 +124,9 @@ def _load_fill():
         L.hkvfill_splitmix.restype = ctypes.c_int
         L.hkvfill_splitmix.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint64,
                                        ctypes.c_uint64, ctypes.c_void_p]
+        L.hkvfill_rows.restype = ctypes.c_int
+        L.hkvfill_rows.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                   ctypes.c_uint64, ctypes.c_uint64, ctypes.c_void_p]
         _fill_lib = L
     return _fill_lib
 
@@ -139,6 +142,49 @@ def gpu_fill(dev_ptr: int, nbytes: int, seed: int, byte_start: int = 0, stream: 
     rc = _load_fill().hkvfill_splitmix(dev_ptr, nbytes, seed & MASK, byte_start // 8, stream)
     if rc != 0:
         raise RuntimeError(f"gpu fill failed with HIP error {rc}")
+
+
+ROW_ZEROS = 1 << 63
+
+
+def gpu_fill_rows(buf, rows: np.ndarray, stream: int = 0) -> None:
+    """Rows of streams at given places in a device uint8 tensor `buf`: rows is
+    an array [n][4] of (byte offset, seed, first word, word count); a count
+    with ROW_ZEROS set writes that many zero words instead.  Rows of one call
+    must not overlap (they run in parallel).  Every row is checked to lie
+    inside the buffer before the launch."""
+    import torch
+    rows = np.ascontiguousarray(rows, dtype=np.uint64).reshape(-1, 4)
+    if rows.shape[0] == 0:
+        return
+    off = rows[:, 0]
+    n_words = rows[:, 3] & np.uint64(ROW_ZEROS - 1)
+    if (off % np.uint64(8)).any():
+        raise ValueError("row offsets must be multiples of 8")
+    if (off + n_words * np.uint64(8) > np.uint64(buf.numel())).any():
+        raise ValueError("a row ends past the buffer")
+    if buf.data_ptr() % 8:
+        raise ValueError("buffer must be 8-byte aligned")
+    # one launch covers at most 2^32 - 1 work items (256 per 64 KiB tile)
+    tiles = max(1, (int(n_words.max()) + 8191) // 8192)
+    per_launch = max(1, (0xFFFFFFFF // 256) // tiles)
+    for lo in range(0, rows.shape[0], per_launch):
+        part = rows[lo:lo + per_launch]
+        dev_rows = torch.from_numpy(np.ascontiguousarray(part).view(np.int64)).to(buf.device)
+        rc = _load_fill().hkvfill_rows(buf.data_ptr(), buf.numel(), dev_rows.data_ptr(),
+                                       part.shape[0], int(n_words.max()), stream)
+        if rc != 0:
+            raise RuntimeError(f"gpu row fill failed with HIP error {rc}")
+        # the table must outlive the launch that reads it
+        if stream:
+            torch.cuda.ExternalStream(stream).synchronize()
+        else:
+            torch.cuda.synchronize()
+        del dev_rows
+    if stream:
+        torch.cuda.ExternalStream(stream).synchronize()
+    else:
+        torch.cuda.synchronize()
 
 
 # --------------------------------------------------------------------------
