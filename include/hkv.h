@@ -152,6 +152,13 @@ typedef struct hkv_layout hkv_layout; /* opaque; its plan is immutable after ini
  * stride.  Object layout: layer-major in model order, then the k blocks of
  * the chunk, real page bytes only, no header; for MLA layers this is an
  * [L_obj][chunk_tokens][mla_width] array.
+ * Defined by: the block size N ("Hybrid Attention Models", Mamba /
+ * Linear-Attention Hybrids, Step 1; "Kimi-Linear" recipe, Note), the chunk
+ * size rule ("Kimi K3" recipe, Why these settings), one block table per KV
+ * group (vLLM hybrid KV-cache blog, section 2.2), the two pool layouts (same
+ * blog, sections 3.1 and 3.2), the balanced KDA groups (Mooncake K3 blog,
+ * "Flat KV") and the separate object groups ("Hybrid Attention Models",
+ * Object-group separation).
  * Errors: HKV_E_ARG, HKV_E_COVER, HKV_E_CHUNK, HKV_E_BATCH, HKV_E_POOL.
  * On success *out owns heap memory released by hkv_layout_destroy. */
 hkv_status hkv_layout_init(const hkv_layout_desc* desc, hkv_layout** out);
@@ -255,7 +262,13 @@ hkv_status hkv_workspace_size(const hkv_layout* layout, int32_t max_chunks, size
 
 /* Store (gather): for every chunk c, layer l and block j < k, copies the
  * page_bytes(l) bytes at pool + pool_offset(l) + block_ids[c][g(l)][j] x
- * stride(l) to objects[c][o(l)] + obj_offset(l) + j x obj_page_bytes(l)
+ * stride(l) to objects[c][o(l)] + obj_offset(l) + j x obj_page_bytes(l).
+ * The source address is the page of a block id in the layer's pool view
+ * (vLLM hybrid KV-cache blog, sections 3.1 and 3.2: a layer's pages sit at
+ * its offset plus block id times its stride); the destination bytes are the
+ * opaque pages of the chunk's object of that layer's object group ("Hybrid
+ * Attention Models", Object-group separation; "Kimi-Linear" recipe: the KDA
+ * state is one opaque page per block).
  * (obj_page_bytes = page_bytes, except KDA pages under kda_codec = 1, which
  * are written in their INT8 form).  Padding and group slack are never read.
  * The pool is not modified.
@@ -288,7 +301,10 @@ hkv_status hkv_store_chunks(const hkv_layout* layout, const void* pool,
                             void* stream);
 
 /* Retrieve (scatter): the inverse copy, objects -> pages of the given,
- * newly allocated block ids.  Writes exactly the real page bytes of the
+ * newly allocated block ids (the engine hands the connector fresh block ids
+ * to load a hit into: "Kimi K3" recipe, AMD MI355X notes; the loaded state
+ * becomes the request's initial state: vLLM hybrid KV-cache blog, section
+ * 5.3; page addresses as for hkv_store_chunks, sections 3.1 and 3.2).  Writes exactly the real page bytes of the
  * addressed pages and nothing else (KDA padding, group slack and every other
  * block are left as they were; a null id writes nothing, and a partial chunk
  * writes only its valid MLA token rows).  Because all groups share one

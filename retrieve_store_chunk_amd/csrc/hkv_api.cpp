@@ -10,6 +10,9 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -25,9 +28,11 @@
 
 struct hkv_layout {
   hkv::Plan plan;
-  // The plan's constant tables (layer placements, then the per-chunk work
-  // items) in the memory of each device the layout has been used on,
-  // uploaded by the first call there and freed with the layout.
+  // The plan's constant tables as the kernels read them: layer placements
+  // (padded to 256 bytes), then the per-chunk work items.
+  std::vector<uint8_t> table_image;
+  // The constant tables in the memory of each device the layout has been
+  // used on, uploaded by the first call there and freed with the layout.
   mutable std::mutex mu;
   mutable std::map<int, void*> dev_tables;
   ~hkv_layout();
@@ -47,12 +52,26 @@ hkv_status hip_error(hipError_t e, const char* what) {
                                   hipGetErrorString(e) + ")");
 }
 
+// HKV_TRACE=1 in the environment: one line on stderr per layout and per
+// call (the layout's N, chunk size and placements; a call's chunks, launches,
+// work items and bytes), like the engine's own log line naming the block size
+// it settled on.
+bool trace_on() {
+  static const bool on = [] {
+    const char* v = std::getenv("HKV_TRACE");
+    return v && *v && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
 // ---------------------------------------------------------------- staging
 // A few pinned host buffers per device, used round-robin.  Each remembers
-// the event recorded after the copy that reads it.
-constexpr int kSlots = 8;
+// the event recorded after the copy that reads it, and has its own lock: a
+// call that must wait for its slot's earlier copy holds only that slot.
+constexpr unsigned kSlots = 8;
 
 struct Slot {
+  std::mutex mu;
   void* host = nullptr;
   size_t cap = 0;
   hipEvent_t done = nullptr;
@@ -60,9 +79,8 @@ struct Slot {
 };
 
 struct Ring {
-  std::mutex mu;
+  std::atomic<unsigned> next{0};
   Slot slot[kSlots];
-  unsigned next = 0;
 };
 
 std::mutex g_rings_mu;
@@ -104,8 +122,8 @@ hkv_status upload(int dev, void* dst, size_t bytes, hipStream_t stream, Fill fil
   DeviceScope scope(dev);
   if (scope.err != hipSuccess) return hip_error(scope.err, "selecting the stream's device");
   Ring* ring = ring_for(dev);
-  std::lock_guard<std::mutex> g(ring->mu);
-  Slot& s = ring->slot[ring->next++ % kSlots];
+  Slot& s = ring->slot[ring->next.fetch_add(1, std::memory_order_relaxed) % kSlots];
+  std::lock_guard<std::mutex> g(s.mu);
   if (s.pending) {
     e = hipEventSynchronize(s.done);
     if (e != hipSuccess) return hip_error(e, "waiting for a staging slot");
@@ -149,6 +167,14 @@ struct Span {
   const char* what;
 };
 
+// Per-thread buffers of the checks, kept from call to call so that a call no
+// larger than the thread's earlier ones allocates nothing on the host either.
+struct CheckBuffers {
+  std::vector<int32_t> ids;
+  std::vector<Span> spans;
+};
+thread_local CheckBuffers t_check;
+
 hkv_status check_disjoint(std::vector<Span>& spans) {
   std::sort(spans.begin(), spans.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
   for (size_t i = 1; i < spans.size(); ++i)
@@ -158,9 +184,112 @@ hkv_status check_disjoint(std::vector<Span>& spans) {
   return HKV_OK;
 }
 
+// The batch's pointers, counts and the engine.  Sets *done for an empty batch.
+hkv_status check_batch_shape(bool store, const hkv_layout* layout, const void* pool,
+                             const hkv_chunk_batch* b, bool* done) {
+  *done = false;
+  if (!layout || !b) return set_error(HKV_E_ARG, "layout and batch must not be NULL");
+  if (b->n_chunks < 0) return set_error(HKV_E_ARG, "n_chunks must be >= 0");
+  if (b->n_chunks == 0) {
+    *done = true;
+    return HKV_OK;
+  }
+  if (!pool || !b->block_ids || !b->objects)
+    return set_error(HKV_E_ARG, "pool, block_ids and objects must not be NULL");
+  const hkv::Plan& p = layout->plan;
+  if (b->engine != HKV_ENGINE_KERNEL && b->engine != HKV_ENGINE_DMA)
+    return set_error(HKV_E_ARG, "engine must be HKV_ENGINE_KERNEL or HKV_ENGINE_DMA");
+  if (b->engine == HKV_ENGINE_DMA && store)
+    return set_error(HKV_E_ARG, "the DMA engine serves retrieves only (a store zero-fills "
+                                "object bytes)");
+  if (b->engine == HKV_ENGINE_DMA && p.kda_codec)
+    return set_error(HKV_E_ARG, "the DMA engine copies bytes; an INT8 layout retrieves "
+                                "through the scatter kernel, which decodes");
+  if ((uint64_t)b->n_chunks * p.items.size() > 0x7FFFFFFFull)
+    return set_error(HKV_E_ARG, "too many tiles in one call; split the batch");
+  return HKV_OK;
+}
+
+// Object pointers, block ids, token counts, distinct retrieve targets, and
+// disjoint buffers (pool, objects and, if given, the workspace span).
+hkv_status check_batch_contents(bool store, const hkv::Plan& p, const void* pool,
+                                const hkv_chunk_batch* b, const void* ws, uint64_t ws_need) {
+  const uint64_t n = (uint64_t)b->n_chunks;
+  const uint64_t G = (uint64_t)p.n_kv_groups, k = (uint64_t)p.blocks_per_chunk;
+  const uint64_t O = (uint64_t)p.n_obj_groups;
+  for (uint64_t i = 0; i < n * O; ++i) {
+    if (!b->objects[i]) return set_error(HKV_E_ARG, "object pointer is NULL");
+    if (!aligned16(b->objects[i]))
+      return set_error(HKV_E_ALIGN, "object pointer is not 16-byte aligned");
+  }
+  const int32_t* ids = b->block_ids;
+  const uint64_t n_ids = n * G * k;
+  for (uint64_t i = 0; i < n_ids; ++i)
+    if (ids[i] != HKV_NULL_BLOCK && (ids[i] < 0 || ids[i] >= p.num_blocks))
+      return set_error(HKV_E_RANGE, "block id " + std::to_string(ids[i]) + " outside [0, " +
+                                        std::to_string(p.num_blocks) + ")");
+  if (b->chunk_tokens)
+    for (uint64_t c = 0; c < n; ++c)
+      if (b->chunk_tokens[c] < 0 || b->chunk_tokens[c] > p.chunk_tokens)
+        return set_error(HKV_E_ARG, "chunk_tokens[" + std::to_string(c) + "] = " +
+                                        std::to_string(b->chunk_tokens[c]) + " outside [0, " +
+                                        std::to_string(p.chunk_tokens) + "]");
+  if (!store) {
+    // One block-id space for all groups: distinct ids <=> disjoint writes.
+    // Null ids write nothing.  Sorting a copy costs O(ids log ids), whatever
+    // the pool's size.
+    std::vector<int32_t>& v = t_check.ids;
+    v.clear();
+    for (uint64_t i = 0; i < n_ids; ++i)
+      if (ids[i] != HKV_NULL_BLOCK) v.push_back(ids[i]);
+    std::sort(v.begin(), v.end());
+    for (size_t i = 1; i < v.size(); ++i)
+      if (v[i] == v[i - 1])
+        return set_error(HKV_E_ALIAS, "retrieve target block id " + std::to_string(v[i]) +
+                                          " appears twice in one call");
+  }
+  std::vector<Span>& spans = t_check.spans;
+  spans.clear();
+  const uintptr_t pb = reinterpret_cast<uintptr_t>(pool);
+  spans.push_back({pb, pb + p.pool_used, "the pool"});
+  if (ws) {
+    const uintptr_t wb = reinterpret_cast<uintptr_t>(ws);
+    spans.push_back({wb, wb + ws_need, "the workspace"});
+  }
+  for (uint64_t c = 0; c < n; ++c)
+    for (uint64_t o = 0; o < O; ++o) {
+      const uintptr_t a = reinterpret_cast<uintptr_t>(b->objects[c * O + o]);
+      if (p.obj_bytes[o]) spans.push_back({a, a + p.obj_bytes[o], "an object"});
+    }
+  return check_disjoint(spans);
+}
+
+// The stream's device and whether the stream is capturing.
+hkv_status stream_state(void* stream, int* dev, bool* capturing) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hkv_status st = stream_device(s, dev);
+  if (st != HKV_OK) return st;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (s) {
+    const hipError_t e = hipStreamIsCapturing(s, &cap);
+    if (e != hipSuccess) return hip_error(e, "querying the stream's capture status");
+  }
+  *capturing = cap != hipStreamCaptureStatusNone;
+  return HKV_OK;
+}
+
 // ---------------------------------------------------------------- layout tables
 constexpr uint64_t layer_table_bytes(const hkv::Plan& p) {
   return hkv::align256(p.dev_layers.size() * sizeof(hkv::DevLayer));
+}
+
+void build_table_image(hkv_layout* lay) {
+  const hkv::Plan& p = lay->plan;
+  const uint64_t lb = layer_table_bytes(p), ib = p.items.size() * sizeof(uint64_t);
+  lay->table_image.assign(lb + ib, 0);
+  std::memcpy(lay->table_image.data(), p.dev_layers.data(),
+              p.dev_layers.size() * sizeof(hkv::DevLayer));
+  std::memcpy(lay->table_image.data() + lb, p.items.data(), ib);
 }
 
 // The layout's constant tables on `dev`: uploaded (synchronously) by the
@@ -177,15 +306,11 @@ hkv_status layout_tables(const hkv_layout* lay, int dev, bool capturing, const u
                                     "synchronously; make one call there before capturing");
   DeviceScope scope(dev);
   if (scope.err != hipSuccess) return hip_error(scope.err, "selecting the stream's device");
-  const hkv::Plan& p = lay->plan;
-  const uint64_t lb = layer_table_bytes(p), ib = p.items.size() * sizeof(uint64_t);
-  std::vector<uint8_t> h(lb + ib, 0);
-  std::memcpy(h.data(), p.dev_layers.data(), p.dev_layers.size() * sizeof(hkv::DevLayer));
-  std::memcpy(h.data() + lb, p.items.data(), ib);
+  const size_t bytes = lay->table_image.size();
   void* d = nullptr;
-  hipError_t e = hipMalloc(&d, lb + ib);
+  hipError_t e = hipMalloc(&d, bytes);
   if (e != hipSuccess) return hip_error(e, "hipMalloc (layout tables)");
-  e = hipMemcpy(d, h.data(), lb + ib, hipMemcpyHostToDevice);
+  e = hipMemcpy(d, lay->table_image.data(), bytes, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(d);
     return hip_error(e, "hipMemcpy (layout tables)");
@@ -237,6 +362,18 @@ hkv_status launch_one(bool store, const hkv::Plan& p, const hkv::CopyArgs& a,
 
 const hkv::InlineTables kNoInlineTables{};
 
+void trace_call(const char* entry, bool store, const hkv::Plan& p, const hkv_chunk_batch* b,
+                uint64_t launches, uint64_t items, const char* tables) {
+  if (!trace_on()) return;
+  std::fprintf(stderr,
+               "[hkv] %s %s: %d chunks, %llu launches, %llu work items (tile %llu B), "
+               "%llu payload bytes, tables %s\n",
+               entry, store ? "store" : "retrieve", b->n_chunks, (unsigned long long)launches,
+               (unsigned long long)items, (unsigned long long)p.tile_bytes,
+               (unsigned long long)((uint64_t)b->n_chunks * (p.obj_bytes[0] + p.obj_bytes[1])),
+               tables);
+}
+
 // The grouped retrieve (hkv_groups.hpp): one upload of every class's tables,
 // then one launch per class.  Sets *done when it took the call.
 hkv_status retrieve_grouped(const hkv::Plan& p, int dev, const void* pool,
@@ -259,31 +396,21 @@ hkv_status retrieve_grouped(const hkv::Plan& p, int dev, const void* pool,
     st = launch_one(false, p, a, kNoInlineTables, stream);
     if (st != HKV_OK) return st;
   }
+  trace_call("hkv_retrieve_chunks", false, p, b, g.launches.size(), g.launched_items,
+             "staged per class");
   return HKV_OK;
 }
 
 hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
                     const hkv_chunk_batch* b, void* ws, size_t ws_bytes, void* stream) {
-  if (!layout || !b) return set_error(HKV_E_ARG, "layout and batch must not be NULL");
-  if (b->n_chunks < 0) return set_error(HKV_E_ARG, "n_chunks must be >= 0");
-  if (b->n_chunks == 0) return HKV_OK;
-  if (!pool || !b->block_ids || !b->objects)
-    return set_error(HKV_E_ARG, "pool, block_ids and objects must not be NULL");
+  bool empty = false;
+  hkv_status st = check_batch_shape(store, layout, pool, b, &empty);
+  if (st != HKV_OK || empty) return st;
   const hkv::Plan& p = layout->plan;
-  if (b->engine != HKV_ENGINE_KERNEL && b->engine != HKV_ENGINE_DMA)
-    return set_error(HKV_E_ARG, "engine must be HKV_ENGINE_KERNEL or HKV_ENGINE_DMA");
-  if (b->engine == HKV_ENGINE_DMA && store)
-    return set_error(HKV_E_ARG, "the DMA engine serves retrieves only (a store zero-fills "
-                                "object bytes)");
-  if (b->engine == HKV_ENGINE_DMA && p.kda_codec)
-    return set_error(HKV_E_ARG, "the DMA engine copies bytes; an INT8 layout retrieves "
-                                "through the scatter kernel, which decodes");
   const uint64_t n = (uint64_t)b->n_chunks;
   const uint64_t G = (uint64_t)p.n_kv_groups, k = (uint64_t)p.blocks_per_chunk;
   const uint64_t O = (uint64_t)p.n_obj_groups;
   const uint64_t per_chunk = p.items.size();
-  if (n * per_chunk > 0x7FFFFFFFull)
-    return set_error(HKV_E_ARG, "too many tiles in one call; split the batch");
   const hkv::WorkspaceLayout wl =
       hkv::workspace_layout(p.dev_layers.size(), per_chunk, n, G, k, O);
   // What hkv_workspace_size(n) promises: room for the grouped retrieve too.
@@ -293,63 +420,20 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
     return set_error(HKV_E_WORKSPACE, "workspace needs " + std::to_string(ws_need) + " bytes");
   if (!aligned16(pool)) return set_error(HKV_E_ALIGN, "pool pointer is not 16-byte aligned");
   if (!aligned16(ws)) return set_error(HKV_E_ALIGN, "workspace is not 16-byte aligned");
-  for (uint64_t i = 0; i < n * O; ++i) {
-    if (!b->objects[i]) return set_error(HKV_E_ARG, "object pointer is NULL");
-    if (!aligned16(b->objects[i]))
-      return set_error(HKV_E_ALIGN, "object pointer is not 16-byte aligned");
-  }
-  const int32_t* ids = b->block_ids;
-  const uint64_t n_ids = n * G * k;
-  for (uint64_t i = 0; i < n_ids; ++i)
-    if (ids[i] != HKV_NULL_BLOCK && (ids[i] < 0 || ids[i] >= p.num_blocks))
-      return set_error(HKV_E_RANGE, "block id " + std::to_string(ids[i]) + " outside [0, " +
-                                        std::to_string(p.num_blocks) + ")");
-  if (b->chunk_tokens)
-    for (uint64_t c = 0; c < n; ++c)
-      if (b->chunk_tokens[c] < 0 || b->chunk_tokens[c] > p.chunk_tokens)
-        return set_error(HKV_E_ARG, "chunk_tokens[" + std::to_string(c) + "] = " +
-                                        std::to_string(b->chunk_tokens[c]) + " outside [0, " +
-                                        std::to_string(p.chunk_tokens) + "]");
-  if (!store) {
-    // One block-id space for all groups: distinct ids <=> disjoint writes.
-    // Null ids write nothing.
-    std::vector<uint8_t> seen((size_t)p.num_blocks, 0);
-    for (uint64_t i = 0; i < n_ids; ++i) {
-      if (ids[i] == HKV_NULL_BLOCK) continue;
-      if (seen[(size_t)ids[i]])
-        return set_error(HKV_E_ALIAS, "retrieve target block id " + std::to_string(ids[i]) +
-                                          " appears twice in one call");
-      seen[(size_t)ids[i]] = 1;
-    }
-  }
-  std::vector<Span> spans;
-  spans.reserve(n * O + 2);
-  const uintptr_t pb = reinterpret_cast<uintptr_t>(pool);
-  spans.push_back({pb, pb + p.pool_used, "the pool"});
-  const uintptr_t wb = reinterpret_cast<uintptr_t>(ws);
-  spans.push_back({wb, wb + ws_need, "the workspace"});
-  for (uint64_t c = 0; c < n; ++c)
-    for (uint64_t o = 0; o < O; ++o) {
-      const uintptr_t a = reinterpret_cast<uintptr_t>(b->objects[c * O + o]);
-      if (p.obj_bytes[o]) spans.push_back({a, a + p.obj_bytes[o], "an object"});
-    }
-  hkv_status st = check_disjoint(spans);
+  st = check_batch_contents(store, p, pool, b, ws, ws_need);
   if (st != HKV_OK) return st;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int dev = 0;
-  st = stream_device(s, &dev);
-  if (st != HKV_OK) return st;
+  bool capturing = false;
   // Under stream capture only what a graph can replay is enqueued: DMA
   // copies between the caller's buffers, or one launch whose tables are in
   // its arguments.  A copy out of a staging slot would replay whatever the
   // ring later put in that slot.
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (s) {
-    const hipError_t e = hipStreamIsCapturing(s, &cap);
-    if (e != hipSuccess) return hip_error(e, "querying the stream's capture status");
-  }
-  const bool capturing = cap != hipStreamCaptureStatusNone;
+  st = stream_state(stream, &dev, &capturing);
+  if (st != HKV_OK) return st;
+  const int32_t* ids = b->block_ids;
+  const uint64_t n_ids = n * G * k;
 
   if (b->engine == HKV_ENGINE_DMA) {
     // One copy per run of pages contiguous in both the object and the pool.
@@ -363,6 +447,9 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
                                           hipMemcpyDefault, s);
       if (e != hipSuccess) return hip_error(e, "hipMemcpyAsync (DMA retrieve)");
     }
+    if (trace_on())
+      std::fprintf(stderr, "[hkv] hkv_retrieve_chunks retrieve (DMA): %d chunks, %zu copies\n",
+                   b->n_chunks, runs.size());
     return HKV_OK;
   }
 
@@ -382,11 +469,16 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   const bool has_tokens = b->chunk_tokens != nullptr;
   hkv::CopyArgs a =
       base_args(p, pool, tables, tables + layer_table_bytes(p), per_chunk, n, has_tokens);
+  const char* entry = store ? "hkv_store_chunks" : "hkv_retrieve_chunks";
   // Per-call tables: in the kernel arguments when they fit (no copy ahead of
   // the launch), else uploaded into the workspace.
   {
     hkv::InlineTables t;
-    if (hkv::pack_inline_tables(p, *b, &t, &a)) return launch_one(store, p, a, t, stream);
+    if (hkv::pack_inline_tables(p, *b, &t, &a)) {
+      st = launch_one(store, p, a, t, stream);
+      if (st == HKV_OK) trace_call(entry, store, p, b, 1, a.total_items, "in the arguments");
+      return st;
+    }
   }
   if (capturing)
     return set_error(HKV_E_CAPTURE, "the call's tables do not fit in the kernel arguments, "
@@ -403,7 +495,9 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   a.ids = reinterpret_cast<const int32_t*>(wsb + wl.ids_off);
   a.objs = reinterpret_cast<const uint64_t*>(wsb + wl.objs_off);
   a.chunk_tokens = reinterpret_cast<const int32_t*>(wsb + wl.tokens_off);
-  return launch_one(store, p, a, kNoInlineTables, stream);
+  st = launch_one(store, p, a, kNoInlineTables, stream);
+  if (st == HKV_OK) trace_call(entry, store, p, b, 1, a.total_items, "staged");
+  return st;
 }
 
 }  // namespace
@@ -433,6 +527,20 @@ hkv_status hkv_layout_init(const hkv_layout_desc* desc, hkv_layout** out) {
   std::string err;
   hkv_status st = hkv::make_plan(*desc, &lay->plan, &err);
   if (st != HKV_OK) return set_error(st, err);
+  build_table_image(lay.get());
+  if (trace_on()) {
+    const hkv::Plan& p = lay->plan;
+    std::fprintf(stderr,
+                 "[hkv] layout: block size N=%lld tokens, chunk C=%lld (k=%d), path %c, "
+                 "%d KV groups, %d object groups, %lld blocks, stride %llu B, pool %llu B used, "
+                 "chunk payload %llu B, %zu work items per chunk (tile %llu B)%s\n",
+                 (long long)p.block_size, (long long)p.chunk_tokens, p.blocks_per_chunk,
+                 p.path == 0 ? 'A' : 'B', p.n_kv_groups, p.n_obj_groups,
+                 (long long)p.num_blocks, (unsigned long long)p.block_stride,
+                 (unsigned long long)p.pool_used,
+                 (unsigned long long)(p.obj_bytes[0] + p.obj_bytes[1]), p.items.size(),
+                 (unsigned long long)p.tile_bytes, p.kda_codec ? ", INT8 KDA codec" : "");
+  }
   *out = lay.release();
   return HKV_OK;
 }

@@ -37,6 +37,26 @@ def test_library_exports_every_declared_function():
         assert hasattr(hkv.lib, n), n
 
 
+PAGE_TITLES = ("Hybrid Attention Models", "Kimi-Linear", "Kimi K3",
+               "vLLM hybrid KV-cache blog", "Mooncake K3 blog")
+
+
+def declaration_comment(name):
+    """The comment block that ends right before `name`'s declaration."""
+    text = open(os.path.join(ROOT, "include", "hkv.h")).read()
+    m = re.search(r"/\*((?:(?!\*/).)*)\*/\s*(?:#define[^\n]*\n\s*)*hkv_status\s+" + name +
+                  r"\s*\(", text, flags=re.S)
+    assert m, name
+    return m.group(1)
+
+
+@pytest.mark.parametrize("name", ["hkv_unified_block_size", "hkv_layout_init",
+                                  "hkv_store_chunks", "hkv_retrieve_chunks"])
+def test_boundary_calls_cite_the_passage_that_defines_them(name):
+    comment = declaration_comment(name)
+    assert any(t in comment for t in PAGE_TITLES), name
+
+
 def test_every_codec_head_dim_has_its_kernel_pair():
     """The launcher runs an INT8 layout on the kernel pair built for its KDA
     head_dim, so every head_dim the planner admits under the codec needs
@@ -213,6 +233,27 @@ def test_call_validation_on_host():
     assert hkv.status_of(hkv.hkv_store_chunks, 0, pool, ids, objs, ws, ws_bytes, 0) \
         == hkv.HKV_E_ARG
     assert "workspace" in hkv.hkv_last_error() or hkv.hkv_last_error() != ""
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake device addresses: host-only check")
+def test_alias_check_cost_does_not_grow_with_the_pool():
+    """A retrieve's repeated-id check sorts the call's ids: a pool of two
+    billion blocks costs a small call nothing (no per-block table)."""
+    import time
+    desc = workloads._desc([0, 0, 0, 1], 1, 4, 4, 1, 1, 128 * (2**31 - 1), mla_width=8)
+    lay = hkv.Layout(desc)
+    assert lay.info["num_blocks"] == 2**31 - 1
+    G, k, O = lay.G, lay.k, lay.O
+    pool = 1 << 40
+    objs = [(1 << 42) + i * 4096 for i in range(2 * O)]
+    ids = np.array([[[2**31 - 2]], [[5]], [[2**31 - 2]], [[7]],
+                    [[11]], [[13]], [[17]], [[19]]], np.int32).reshape(2, G, k)
+    t0 = time.perf_counter()
+    for _ in range(200):
+        assert hkv.status_of(hkv.hkv_retrieve_chunks, lay.handle, pool, ids, objs, 1 << 43,
+                             lay.workspace_size(2), 0) == hkv.HKV_E_ALIAS
+    assert time.perf_counter() - t0 < 2.0
+    assert "appears twice" in hkv.hkv_last_error()
 
 
 def test_calls_past_the_item_limit_are_rejected_before_any_hip_call():
