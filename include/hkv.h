@@ -318,6 +318,47 @@ hkv_status hkv_retrieve_chunks(const hkv_layout* layout, void* pool,
                                const hkv_chunk_batch* batch, void* workspace,
                                size_t ws_bytes, void* stream);
 
+#define HKV_OP_STORE 0
+#define HKV_OP_RETRIEVE 1
+
+/* For callers that cannot allocate memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): hkv_store_chunks
+ * (op = HKV_OP_STORE) or hkv_retrieve_chunks (op = HKV_OP_RETRIEVE) with the
+ * same kernels and the same bytes in the pool and objects, but no workspace
+ * and no allocation.  It calls no hipMalloc, hipFree, hipHostMalloc or other
+ * allocating routine, and uses no pinned staging.
+ *   - The layout's constant tables live in a static device array of the
+ *     library, 4 MiB per device (held from the first such call on a device
+ *     until the process ends); a layout whose tables are larger (more than
+ *     about 500,000 work items per chunk) gets HKV_E_WORKSPACE.
+ *   - The array holds one layout's tables at a time.  A call whose layout's
+ *     tables are not there copies them in from the layout's host memory and
+ *     waits for `stream` to finish; later calls with the same layout on that
+ *     device enqueue without waiting.  While `stream` is capturing, such a
+ *     copy is refused (HKV_E_CAPTURE, nothing enqueued); a captured call
+ *     reads the array when the graph replays, so no call with another layout
+ *     may run on that device between capture and replay.
+ *   - The call's block ids, object addresses and token counts travel in
+ *     kernel arguments: one launch per run of chunks that fits (up to 96
+ *     chunks at the Kimi-Linear shapes), so a large call is several launches.
+ *   - Every call on a device shares that device's array: calls that overlap
+ *     on one device (other streams, other threads) with different layouts
+ *     race, and must be ordered by the caller.
+ *   - A retrieve with null ids or partial chunks runs one launch over every
+ *     work item per run of chunks (no per-class launches); the bytes written
+ *     are the same.
+ * pool: DEVICE as for hkv_store_chunks (written only by a retrieve).
+ * batch: as for hkv_store_chunks; engine must be HKV_ENGINE_KERNEL.
+ * Host-side checks keep per-thread buffers between calls, so a call no
+ * larger than the thread's earlier ones does not allocate host memory either.
+ * Errors: HKV_E_ARG (also a bad op, the DMA engine, or a chunk whose ids and
+ * object addresses alone exceed the kernel-argument block), HKV_E_RANGE,
+ * HKV_E_ALIAS (objects overlap each other or the pool; repeated retrieve
+ * ids), HKV_E_ALIGN, HKV_E_WORKSPACE (tables larger than the static array),
+ * HKV_E_CAPTURE, HKV_E_HIP. */
+hkv_status hkv_move_chunks_noalloc(const hkv_layout* layout, int32_t op, void* pool,
+                                   const hkv_chunk_batch* batch, void* stream);
+
 /* ------------------------------------------------------------------------
  * Object identity.  Cached pages are byte-opaque, so an entry must never be
  * read back by an engine whose object format differs: other attention

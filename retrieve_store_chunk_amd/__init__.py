@@ -77,6 +77,9 @@ class hkv_chunk_batch(ctypes.Structure):
 HKV_ENGINE_KERNEL = 0
 HKV_ENGINE_DMA = 1
 
+HKV_OP_STORE = 0
+HKV_OP_RETRIEVE = 1
+
 
 def one_hip_runtime() -> None:
     """A process must hold one HIP runtime.  PyTorch-ROCm ships its own copy,
@@ -115,6 +118,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     L.hkv_retrieve_chunks.restype = i32
     L.hkv_retrieve_chunks.argtypes = [vp, vp, ctypes.POINTER(hkv_chunk_batch), vp,
                                       ctypes.c_size_t, vp]
+    L.hkv_move_chunks_noalloc.restype = i32
+    L.hkv_move_chunks_noalloc.argtypes = [vp, i32, vp, ctypes.POINTER(hkv_chunk_batch), vp]
     L.hkv_layout_fingerprint.restype = i32
     L.hkv_layout_fingerprint.argtypes = [vp, ctypes.POINTER(u64)]
     L.hkv_chunk_keys.restype = i32
@@ -287,6 +292,17 @@ def hkv_retrieve_chunks(handle: int, pool_ptr: int, block_ids, objects, workspac
     del keep
 
 
+def hkv_move_chunks_noalloc(handle: int, op: int, pool_ptr: int, block_ids, objects,
+                            stream: int = 0, info: dict | None = None,
+                            chunk_tokens=None) -> None:
+    """op: HKV_OP_STORE or HKV_OP_RETRIEVE.  No workspace: the library keeps
+    the layout's tables in its static device scratch."""
+    b, keep = _batch(handle, block_ids, objects, info, chunk_tokens, HKV_ENGINE_KERNEL)
+    _check(lib.hkv_move_chunks_noalloc(handle, op, pool_ptr, ctypes.byref(b), stream),
+           "hkv_move_chunks_noalloc")
+    del keep
+
+
 def status_of(fn, *args) -> int:
     """Calls one of the wrappers above and returns its status instead of
     raising (for tests of error paths)."""
@@ -343,3 +359,7 @@ class Layout:
                  chunk_tokens=None, engine=HKV_ENGINE_KERNEL):
         hkv_retrieve_chunks(self.handle, pool_ptr, block_ids, objects, ws_ptr, ws_bytes, stream,
                             info=self.info, chunk_tokens=chunk_tokens, engine=engine)
+
+    def move_noalloc(self, op, pool_ptr, block_ids, objects, stream=0, chunk_tokens=None):
+        hkv_move_chunks_noalloc(self.handle, op, pool_ptr, block_ids, objects, stream,
+                                info=self.info, chunk_tokens=chunk_tokens)

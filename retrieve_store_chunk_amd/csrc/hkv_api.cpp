@@ -7,6 +7,10 @@
 // caller's workspace on the same stream first.  No call synchronises the
 // stream; a staging slot is reused only after the event recorded behind its
 // copy has completed.
+//
+// hkv_move_chunks_noalloc runs the same kernels without any allocation: the
+// layout's tables go into a static device array (hkv_copy.hip) and the
+// call's tables into kernel arguments, several launches if need be.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -31,6 +35,9 @@ struct hkv_layout {
   // The plan's constant tables as the kernels read them: layer placements
   // (padded to 256 bytes), then the per-chunk work items.
   std::vector<uint8_t> table_image;
+  // Never reused by another layout of the process: names the tables that the
+  // static scratch of hkv_move_chunks_noalloc holds.
+  uint64_t serial = 0;
   // The constant tables in the memory of each device the layout has been
   // used on, uploaded by the first call there and freed with the layout.
   mutable std::mutex mu;
@@ -500,6 +507,113 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   return st;
 }
 
+// ---------------------------------------------------------------- no allocation
+// Which layout's tables the static scratch of each device holds (its serial;
+// 0 = none yet).  Calls that overlap on one device race for the scratch, as
+// the header says.
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+uint64_t g_scratch_holds[kMaxScratchDevices] = {};
+std::atomic<uint64_t> g_next_serial{1};
+
+// The most chunks of a call whose block ids, object addresses and token
+// counts fit in one launch's kernel arguments.
+uint64_t inline_chunks_per_launch(const hkv::Plan& p, bool has_tokens) {
+  const uint64_t ids = (uint64_t)p.n_kv_groups * (uint64_t)p.blocks_per_chunk;
+  const uint64_t O = (uint64_t)p.n_obj_groups;
+  auto words = [&](uint64_t m) {
+    return (m * ids * sizeof(int32_t) + 7) / 8 + m * O +
+           (has_tokens ? (m * sizeof(int32_t) + 7) / 8 : 0);
+  };
+  uint64_t m = hkv::kInlineWords;  // an upper bound: a chunk takes at least one word
+  while (m > 0 && words(m) > hkv::kInlineWords) --m;
+  return m;
+}
+
+hkv_status move_noalloc(bool store, const hkv_layout* layout, void* pool,
+                        const hkv_chunk_batch* b, void* stream) {
+  bool empty = false;
+  hkv_status st = check_batch_shape(store, layout, pool, b, &empty);
+  if (st != HKV_OK || empty) return st;
+  if (b->engine != HKV_ENGINE_KERNEL)
+    return set_error(HKV_E_ARG, "hkv_move_chunks_noalloc runs the kernels only "
+                                "(engine must be HKV_ENGINE_KERNEL)");
+  const hkv::Plan& p = layout->plan;
+  const bool has_tokens = b->chunk_tokens != nullptr;
+  const uint64_t per_launch = inline_chunks_per_launch(p, has_tokens);
+  if (per_launch == 0)
+    return set_error(HKV_E_ARG, "one chunk's block ids and object addresses exceed the "
+                                "kernel-argument block");
+  const uint64_t table_bytes = layout->table_image.size();
+  if (table_bytes > hkv::kStaticScratchBytes)
+    return set_error(HKV_E_WORKSPACE, "the layout's tables need " + std::to_string(table_bytes) +
+                                          " bytes; the static scratch holds " +
+                                          std::to_string(hkv::kStaticScratchBytes));
+  if (!aligned16(pool)) return set_error(HKV_E_ALIGN, "pool pointer is not 16-byte aligned");
+  st = check_batch_contents(store, p, pool, b, nullptr, 0);
+  if (st != HKV_OK) return st;
+
+  int dev = 0;
+  bool capturing = false;
+  st = stream_state(stream, &dev, &capturing);
+  if (st != HKV_OK) return st;
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return set_error(HKV_E_ARG, "device index beyond the static scratch's device table");
+  uint8_t* scratch = nullptr;
+  {
+    DeviceScope scope(dev);
+    if (scope.err != hipSuccess) return hip_error(scope.err, "selecting the stream's device");
+    const int e = hkv::static_scratch(dev, &scratch);
+    if (e != 0) return hip_error((hipError_t)e, "hipGetSymbolAddress (static scratch)");
+  }
+  {
+    // The layout's tables into the scratch, unless it holds them already.
+    // The source is the layout's own host image; the stream is then drained
+    // so that work on any other stream sees the tables whole.
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (g_scratch_holds[dev] != layout->serial) {
+      if (capturing)
+        return set_error(HKV_E_CAPTURE, "the static scratch holds another layout's tables; "
+                                        "make one call with this layout before capturing");
+      g_scratch_holds[dev] = 0;
+      hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+      DeviceScope scope(dev);
+      if (scope.err != hipSuccess) return hip_error(scope.err, "selecting the stream's device");
+      hipError_t e = hipMemcpyAsync(scratch, layout->table_image.data(), table_bytes,
+                                    hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return hip_error(e, "hipMemcpyAsync (tables into the scratch)");
+      e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return hip_error(e, "hipStreamSynchronize (tables into the scratch)");
+      g_scratch_holds[dev] = layout->serial;
+    }
+  }
+  const uint64_t n = (uint64_t)b->n_chunks;
+  const uint64_t Gk = (uint64_t)p.n_kv_groups * (uint64_t)p.blocks_per_chunk;
+  const uint64_t O = (uint64_t)p.n_obj_groups;
+  const uint8_t* layers = scratch;
+  const uint8_t* items = scratch + layer_table_bytes(p);
+  uint64_t launches = 0;
+  for (uint64_t c0 = 0; c0 < n; c0 += per_launch) {
+    const uint64_t m = std::min(per_launch, n - c0);
+    hkv_chunk_batch part{};
+    part.n_chunks = (int32_t)m;
+    part.block_ids = b->block_ids + c0 * Gk;
+    part.objects = b->objects + c0 * O;
+    part.chunk_tokens = has_tokens ? b->chunk_tokens + c0 : nullptr;
+    part.engine = HKV_ENGINE_KERNEL;
+    hkv::CopyArgs a = base_args(p, pool, layers, items, p.items.size(), m, has_tokens);
+    hkv::InlineTables t;
+    if (!hkv::pack_inline_tables(p, part, &t, &a))
+      return set_error(HKV_E_ARG, "internal: a launch's tables do not fit its arguments");
+    st = launch_one(store, p, a, t, stream);
+    if (st != HKV_OK) return st;
+    ++launches;
+  }
+  trace_call("hkv_move_chunks_noalloc", store, p, b, launches, n * p.items.size(),
+             "in the arguments; layout tables in the static scratch");
+  return HKV_OK;
+}
+
 }  // namespace
 
 hkv_layout::~hkv_layout() {
@@ -528,6 +642,7 @@ hkv_status hkv_layout_init(const hkv_layout_desc* desc, hkv_layout** out) {
   hkv_status st = hkv::make_plan(*desc, &lay->plan, &err);
   if (st != HKV_OK) return set_error(st, err);
   build_table_image(lay.get());
+  lay->serial = g_next_serial.fetch_add(1, std::memory_order_relaxed);
   if (trace_on()) {
     const hkv::Plan& p = lay->plan;
     std::fprintf(stderr,
@@ -616,6 +731,13 @@ hkv_status hkv_retrieve_chunks(const hkv_layout* layout, void* pool,
                                const hkv_chunk_batch* batch, void* workspace, size_t ws_bytes,
                                void* stream) {
   return run_copy(false, layout, pool, batch, workspace, ws_bytes, stream);
+}
+
+hkv_status hkv_move_chunks_noalloc(const hkv_layout* layout, int32_t op, void* pool,
+                                   const hkv_chunk_batch* batch, void* stream) {
+  if (op != HKV_OP_STORE && op != HKV_OP_RETRIEVE)
+    return set_error(HKV_E_ARG, "op must be HKV_OP_STORE or HKV_OP_RETRIEVE");
+  return move_noalloc(op == HKV_OP_STORE, layout, pool, batch, stream);
 }
 
 hkv_status hkv_layout_fingerprint(const hkv_layout* layout, uint64_t* out) {

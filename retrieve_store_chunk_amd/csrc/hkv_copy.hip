@@ -35,8 +35,17 @@
 // of bf16/fp8 values pass unchanged.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "hkv_device_tables.hpp"
 #include "hkv_launch.hpp"
+
+// The no-allocation entry point's scratch: a layout's tables (layer
+// placements, work items) live here instead of in memory the library
+// allocates.  Host code never names it after the lookup in
+// hkv::static_scratch: on the host the name is only a stand-in for the
+// symbol, not a device address.
+static __device__ __align__(256) uint8_t scratch[hkv::kStaticScratchBytes];
 
 #define HKV_GLOBAL __attribute__((address_space(1)))
 #define HKV_CONST __attribute__((address_space(4)))
@@ -363,6 +372,23 @@ HKV_KERNEL_PAIR(_int8_d256, 256)
 #undef HKV_KERNEL_PAIR
 
 namespace hkv {
+
+int static_scratch(int dev, uint8_t** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static uint8_t* addr[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    // Each device holds its own copy of the array at its own address.
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    addr[dev] = static_cast<uint8_t*>(p);
+  }
+  *ptr = addr[dev];
+  return 0;
+}
 
 int launch_copy(bool store, const CopyArgs& a, const InlineTables& t, uint32_t grid,
                 void* stream) {

@@ -32,7 +32,7 @@ def header_functions():
 def test_library_exports_every_declared_function():
     names = header_functions()
     assert {"hkv_unified_block_size", "hkv_layout_init", "hkv_store_chunks",
-            "hkv_retrieve_chunks"} <= set(names)
+            "hkv_retrieve_chunks", "hkv_move_chunks_noalloc"} <= set(names)
     for n in names:
         assert hasattr(hkv.lib, n), n
 
@@ -233,6 +233,56 @@ def test_call_validation_on_host():
     assert hkv.status_of(hkv.hkv_store_chunks, 0, pool, ids, objs, ws, ws_bytes, 0) \
         == hkv.HKV_E_ARG
     assert "workspace" in hkv.hkv_last_error() or hkv.hkv_last_error() != ""
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="fake device addresses: host-only check")
+def test_noalloc_validation_on_host():
+    """hkv_move_chunks_noalloc checks its arguments like the workspace entry
+    points, before any HIP call; fake addresses are safe here."""
+    lay = hkv.Layout(workloads.make_config("tiny").desc)
+    G, k, O = lay.G, lay.k, lay.O
+    nb = lay.info["num_blocks"]
+    pool = 1 << 40
+    used = lay.info["pool_bytes_used"]
+    objs = [pool + (1 << 30) + i * (1 << 20) for i in range(2 * O)]
+    ids = np.arange(2 * G * k, dtype=np.int32).reshape(2, G, k)
+    fn = hkv.hkv_move_chunks_noalloc
+
+    def st(op, **kw):
+        a = dict(pool=pool, ids=ids, objs=objs, tokens=None)
+        a.update(kw)
+        return hkv.status_of(fn, lay.handle, op, a["pool"], a["ids"], a["objs"], 0, None,
+                             a["tokens"])
+
+    for op in (hkv.HKV_OP_STORE, hkv.HKV_OP_RETRIEVE):
+        assert st(op, pool=pool + 8) == hkv.HKV_E_ALIGN
+        assert st(op, objs=[objs[0] + 1] + objs[1:]) == hkv.HKV_E_ALIGN
+        assert st(op, objs=[0] + objs[1:]) == hkv.HKV_E_ARG
+        bad = ids.copy()
+        bad[1, 0, 0] = nb
+        assert st(op, ids=bad) == hkv.HKV_E_RANGE
+        assert st(op, tokens=[1, lay.info["chunk_tokens"] + 1]) == hkv.HKV_E_ARG
+        assert st(op, objs=[objs[0]] * len(objs)) == hkv.HKV_E_ALIAS
+        assert st(op, objs=[pool + used - 256] + objs[1:]) == hkv.HKV_E_ALIAS
+        assert hkv.status_of(fn, lay.handle, op, 0, np.zeros((0, G, k), np.int32), [],
+                             0) == hkv.HKV_OK
+    dup = ids.copy()
+    dup[1, 0, 0] = dup[0, 0, 0]
+    assert st(hkv.HKV_OP_RETRIEVE, ids=dup) == hkv.HKV_E_ALIAS
+    assert st(2) == hkv.HKV_E_ARG and "op must be" in hkv.hkv_last_error()
+    # the DMA engine is not served (the wrapper always asks for the kernels)
+    b, keep = hkv._batch(lay.handle, ids, objs, lay.info, None, hkv.HKV_ENGINE_DMA)
+    import ctypes
+    assert hkv.lib.hkv_move_chunks_noalloc(lay.handle, hkv.HKV_OP_RETRIEVE, pool,
+                                           ctypes.byref(b), None) == hkv.HKV_E_ARG
+    del keep
+    # tables larger than the static scratch: k = 40 blocks per chunk at the
+    # Kimi-Linear TP=1 shapes is 572,680 work items (4.6 MB of tables)
+    big = hkv.Layout(dict(workloads.make_config("kl_tp1").desc, chunk_min_tokens=40 * 1888))
+    bids = np.zeros((1, big.G, big.k), np.int32)
+    assert hkv.status_of(fn, big.handle, hkv.HKV_OP_STORE, pool, bids, objs[:big.O], 0,
+                         big.info) == hkv.HKV_E_WORKSPACE
+    assert "static scratch" in hkv.hkv_last_error()
 
 
 @pytest.mark.skipif(_gpu_visible(), reason="fake device addresses: host-only check")

@@ -1,0 +1,219 @@
+"""GPU: hkv_move_chunks_noalloc against hkv_store_chunks / hkv_retrieve_chunks.
+
+Every case runs the same calls through both entry points on twin buffers
+(same seeded pool and object bytes) and compares the whole pool and every
+object byte for byte after each call: two stores in a row, the second
+smaller, then two retrieves in a row, the second smaller.  The cases cover
+calls that need several launches (more chunks than one launch's kernel
+arguments hold), null ids and partial chunks, the INT8 codec, and layouts
+that take turns on the static scratch (its tables are copied in again).
+The tiny workload is also checked against the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _align(x, a=256):
+    return (x + a - 1) // a * a
+
+
+class Twin:
+    """One layout, two pools and two sets of object slots with equal bytes:
+    side 0 goes through the workspace entry points, side 1 through the
+    no-allocation one."""
+
+    def __init__(self, desc, n_slots, seed):
+        import retrieve_store_chunk_amd as hkv
+        self.hkv = hkv
+        self.lay = hkv.Layout(desc)
+        info = self.lay.info
+        self.info = info
+        self.used = info["pool_bytes_used"]
+        self.obj_stride = [_align(max(1, info["obj_bytes"][o])) for o in range(self.lay.O)]
+        # equal seeded bytes on both sides (the counter-based generator, on the GPU)
+        self.pools = [torch.empty(_align(self.used), dtype=torch.uint8, device="cuda")
+                      for _ in range(2)]
+        for p in self.pools:
+            W.gpu_fill(p.data_ptr(), p.numel(), W.derive_seed(seed, 1))
+        self.objs = []
+        for side in range(2):
+            row = []
+            for o in range(self.lay.O):
+                a = torch.empty(n_slots * self.obj_stride[o], dtype=torch.uint8, device="cuda")
+                W.gpu_fill(a.data_ptr(), a.numel(), W.derive_seed(seed, 2, o))
+                row.append(a)
+            self.objs.append(row)
+        self.n_slots = n_slots
+        self.ws_bytes = self.lay.workspace_size(n_slots)
+        self.ws = torch.empty(max(256, self.ws_bytes), dtype=torch.uint8, device="cuda")
+        self.stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+
+    def ptrs(self, side, slots):
+        return [self.objs[side][o].data_ptr() + s * self.obj_stride[o]
+                for s in slots for o in range(self.lay.O)]
+
+    def call(self, op, ids, slots, tokens=None, noalloc_first=True):
+        """The same call on both sides, then a byte-for-byte comparison."""
+        hkv = self.hkv
+        s = self.stream.cuda_stream
+        order = (1, 0) if noalloc_first else (0, 1)
+        for side in order:
+            pool = self.pools[side].data_ptr()
+            if side == 1:
+                code = hkv.HKV_OP_STORE if op == "store" else hkv.HKV_OP_RETRIEVE
+                self.lay.move_noalloc(code, pool, ids, self.ptrs(1, slots), s,
+                                      chunk_tokens=tokens)
+            elif op == "store":
+                self.lay.store(pool, ids, self.ptrs(0, slots), self.ws.data_ptr(),
+                               self.ws_bytes, s, chunk_tokens=tokens)
+            else:
+                self.lay.retrieve(pool, ids, self.ptrs(0, slots), self.ws.data_ptr(),
+                                  self.ws_bytes, s, chunk_tokens=tokens)
+        self.stream.synchronize()
+        assert torch.equal(self.pools[0], self.pools[1]), f"{op}: pools differ"
+        for o in range(self.lay.O):
+            assert torch.equal(self.objs[0][o], self.objs[1][o]), f"{op}: objects {o} differ"
+
+
+def _ids(rng, n, G, k, num_blocks, distinct, null_frac=0.0):
+    if distinct:
+        ids = rng.permutation(num_blocks)[: n * G * k].astype(np.int32)
+    else:
+        ids = rng.integers(0, num_blocks, size=n * G * k).astype(np.int32)
+    if null_frac:
+        ids[rng.random(ids.size) < null_frac] = -1
+    return ids.reshape(n, G, k)
+
+
+def _tokens(rng, n, C, partial):
+    if not partial:
+        return None
+    t = np.full(n, C, dtype=np.int32)
+    sel = rng.random(n) < 0.5
+    t[sel] = rng.integers(0, C + 1, size=int(sel.sum()))
+    return t
+
+
+def run_case(desc, seed, n_store, n_retrieve, null_frac=0.0, partial=False,
+             store_repeats=False):
+    """Store n_store[0] then n_store[1] chunks, retrieve n_retrieve[0] then
+    n_retrieve[1] chunks, each call on both entry points."""
+    rng = np.random.default_rng(seed)
+    n_slots = max(max(n_store), max(n_retrieve))
+    t = Twin(desc, n_slots, seed)
+    G, k = t.lay.G, t.lay.k
+    nb, C = t.info["num_blocks"], t.info["chunk_tokens"]
+    _log(f"[noalloc] case seed={seed:#x} blocks={nb} G={G} k={k} store={n_store} "
+         f"retrieve={n_retrieve} nulls={null_frac} partial={partial}")
+    for i, n in enumerate(n_store):
+        ids = _ids(rng, n, G, k, nb, distinct=not store_repeats, null_frac=null_frac)
+        t.call("store", ids, list(range(n)), _tokens(rng, n, C, partial),
+               noalloc_first=(i == 0))
+    for i, n in enumerate(n_retrieve):
+        ids = _ids(rng, n, G, k, nb, distinct=True, null_frac=null_frac)
+        t.call("retrieve", ids, list(range(n)), _tokens(rng, n, C, partial),
+               noalloc_first=(i == 0))
+    return t
+
+
+def many_blocks_desc():
+    # 4 layers KKKM, 88-byte KDA pages and 128-byte MLA pages, path B: a
+    # 1 MiB pool holds 8192 blocks, so one retrieve can take 2000 chunks
+    # (21 launches of 96).
+    return W._desc([0, 0, 0, 1], 1, 4, 4, 1, 1, 1 << 20, mla_width=8)
+
+
+def codec_desc():
+    # INT8 codec, head_dim 16: 2 heads x 16 x 16 fp32 + (96, 3) bf16; path B,
+    # 910 blocks of 18,432 bytes.
+    return W._desc([0, 0, 0, 1], 2, 16, 96, 2, 1, 16 << 20, kda_codec=1)
+
+
+def test_noalloc_matches_workspace_entry_points_tiny():
+    run_case(W.make_config("tiny").desc, 0x5EED01, n_store=(300, 40), n_retrieve=(16, 5),
+             store_repeats=True)
+
+
+def test_noalloc_kimi_linear_tp1_shapes():
+    cfg = W.make_small_config("kl_tp1")
+    run_case(cfg.desc, 0x5EED02, n_store=(17, 5), n_retrieve=(17, 3))
+
+
+def test_noalloc_k3_holes_and_tails():
+    cfg = W.make_small_config("k3_tp8_holes")
+    cfg.desc["pool_bytes"] = 2 << 30  # 202 blocks: 20 chunks of 8 distinct ids
+    run_case(cfg.desc, 0x5EED03, n_store=(20, 7), n_retrieve=(20, 6), null_frac=0.4,
+             partial=True)
+
+
+def test_noalloc_several_launches_per_call():
+    run_case(many_blocks_desc(), 0x5EED04, n_store=(2000, 150), n_retrieve=(2000, 150))
+    run_case(many_blocks_desc(), 0x5EED05, n_store=(700, 97), n_retrieve=(1500, 96),
+             null_frac=0.2, partial=True)
+
+
+def test_noalloc_int8_codec():
+    run_case(codec_desc(), 0x5EED06, n_store=(200, 30), n_retrieve=(150, 20))
+
+
+def test_noalloc_layouts_take_turns_on_the_scratch():
+    """Alternating layouts: each call whose layout's tables are not in the
+    scratch copies them in again; results stay equal."""
+    a = Twin(W.make_config("tiny").desc, 8, 0x5EED07)
+    b = Twin(many_blocks_desc(), 8, 0x5EED08)
+    rng = np.random.default_rng(0x5EED09)
+    for step in range(3):
+        for t in (a, b, a):
+            nb = t.info["num_blocks"]
+            t.call("store", _ids(rng, 8, t.lay.G, t.lay.k, nb, distinct=False),
+                   list(range(8)))
+            t.call("retrieve", _ids(rng, 3, t.lay.G, t.lay.k, nb, distinct=True), [0, 1, 2])
+
+
+def test_noalloc_oracle_round_trip_tiny():
+    """The no-allocation entry point alone against the oracle."""
+    import retrieve_store_chunk_amd as hkv
+    cfg = W.make_config("tiny")
+    lay = hkv.Layout(cfg.desc)
+    ref = oracle.Layout(cfg.desc)
+    used = ref.summary["pool_bytes_used"]
+    pool_ref = W.fill_bytes(0xABC, 0, used)
+    pool = torch.from_numpy(pool_ref).to("cuda")
+    rng = np.random.default_rng(0x5EED0A)
+    n = 12
+    ids = _ids(rng, n, ref.G, ref.k, ref.summary["num_blocks"], distinct=True)
+    objs = [[torch.zeros(ref.obj_bytes(o), dtype=torch.uint8, device="cuda")
+             for o in range(ref.O)] for _ in range(n)]
+    objs_ref = [[np.zeros(ref.obj_bytes(o), np.uint8) for o in range(ref.O)] for _ in range(n)]
+    ptrs = [objs[c][o].data_ptr() for c in range(n) for o in range(ref.O)]
+    lay.move_noalloc(hkv.HKV_OP_STORE, pool.data_ptr(), ids, ptrs)
+    ref.store(pool_ref, ids, objs_ref)
+    ids2 = _ids(rng, n, ref.G, ref.k, ref.summary["num_blocks"], distinct=True)
+    lay.move_noalloc(hkv.HKV_OP_RETRIEVE, pool.data_ptr(), ids2, ptrs)
+    ref.retrieve(pool_ref, ids2, objs_ref)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool.cpu().numpy(), pool_ref)
+    for c in range(n):
+        for o in range(ref.O):
+            assert np.array_equal(objs[c][o].cpu().numpy(), objs_ref[c][o])
