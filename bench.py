@@ -22,13 +22,21 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 HOST_LINK_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction (32 GT/s x 16 lanes, 128b/130b)
-METRIC = "store+retrieve GB/s of KV/state pages (Kimi-Linear shapes, N=1888); % HBM peak"
+HOST_SHARE_THREADS = 16  # host threads per GPU of the machine (the CPU leg's cap)
 CSRC = os.path.join(ROOT, "retrieve_store_chunk_amd", "csrc")
 KERNEL_SOURCES = ("hkv_copy.hip", "hkv_device_tables.hpp", "hkv_launch.hpp", "hkv_plan.cpp")
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def metric_for(cfg, block_size: int, on_host: bool) -> str:
+    """The metric line of a workload: its shapes and block size, against HBM
+    peak (or the host link's, for objects in pinned host memory).  For the
+    Kimi-Linear TP=1 workload this is the headline metric."""
+    peak = "% host-link peak" if on_host else "% HBM peak"
+    return f"store+retrieve GB/s of KV/state pages ({cfg.shapes}, N={block_size}); {peak}"
 
 
 def kernel_source_sha() -> str:
@@ -83,14 +91,36 @@ def wave_bytes(layout, w) -> tuple:
     return data, n * info["chunk_payload_bytes"], live
 
 
-def cpu_threads() -> int:
-    """Host threads for the threaded oracle leg: the CPUs this process may
-    use, at most 16 (one GPU's share of a host)."""
+def cpu_available() -> int:
+    """The CPUs this process may run on."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        return os.cpu_count() or 1
+
+
+def cpu_threads() -> int:
+    """Host threads for the threaded oracle leg: every CPU this process may
+    use, at most one GPU's share of the host (HOST_SHARE_THREADS)."""
+    return max(1, min(HOST_SHARE_THREADS, cpu_available()))
+
+
+def seeded_fill(arrays, seeds, threads: int) -> None:
+    """Fills each uint8 array with its seed's counter-based stream (the same
+    generator as the GPU inputs), in 64 MiB pieces on `threads` threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import workloads as W
+    piece = 64 << 20
+    jobs = [(a, seed, lo) for a, seed in zip(arrays, seeds) for lo in range(0, a.size, piece)]
+
+    def run(job):
+        a, seed, lo = job
+        hi = min(a.size, lo + piece)
+        a[lo:hi] = W.fill_bytes(seed, lo, hi - lo)
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(run, jobs))
 
 
 def cpu_baseline(cfg, threads: int = 1, min_seconds: float = 10.0,
@@ -116,9 +146,15 @@ def cpu_baseline(cfg, threads: int = 1, min_seconds: float = 10.0,
     desc["pool_bytes"] = per_block * (n_store * ids_per_chunk + 1)
     lay = oracle.Layout(desc)
     s = lay.summary
-    pool = np.full(s["pool_bytes_used"], 0x5A, np.uint8)
-    objs = [[np.full(lay.obj_bytes(o), 0xA5, np.uint8) for o in range(lay.O)]
+    # seeded bytes from the inputs' generator (the pool's and the objects'
+    # streams of the workload's seed)
+    pool = np.empty(s["pool_bytes_used"], np.uint8)
+    objs = [[np.empty(lay.obj_bytes(o), np.uint8) for o in range(lay.O)]
             for _ in range(n_store)]
+    seeded_fill([pool] + [a for row in objs for a in row],
+                [W.initial_pool_seed(cfg)] + [W.derive_seed(W.object_seed(cfg, 0, c), o)
+                                              for c in range(n_store) for o in range(lay.O)],
+                cpu_threads())
     perm = W.permutation(W.derive_seed(cfg.seed, 1234), s["num_blocks"])
     store_ids = perm[: n_store * ids_per_chunk].reshape(n_store, lay.G, lay.k)
     perm2 = W.permutation(W.derive_seed(cfg.seed, 1235), s["num_blocks"])
@@ -150,9 +186,11 @@ def cpu_baseline(cfg, threads: int = 1, min_seconds: float = 10.0,
             passes += 1
     gbs = passes * payload / t_wall / 1e9
     how = "single-threaded" if threads == 1 else f"{threads} host threads, chunks split evenly"
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads,
+            "cores_available": cpu_available(), "kind": "oracle",
             "sample": f"{passes} passes of: store {n_store} chunks + retrieve {n_ret} chunks "
-                      f"(same page shapes, pool of {s['num_blocks']} blocks); "
+                      f"(same page shapes, pool of {s['num_blocks']} blocks, pool and object "
+                      f"bytes from the workload's seeded generator); "
                       f"{passes * payload / 1e9:.1f} GB moved in {t_wall:.1f} s wall, "
                       f"{how}, plain C memcpy"
                       + (" + per-row INT8 codec of KDA pages" if s["kda_codec"] else "")}
@@ -272,15 +310,20 @@ def build_parser() -> argparse.ArgumentParser:
                     help="capture one step's calls into a HIP graph after the warm-up and "
                          "time its replays (every call's tables must fit in its kernel "
                          "arguments; one-stream workloads only)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the reference rates timed after the steps by default: torch "
+                         "copy_ of one 8 GiB buffer (the achievable device copy, also the "
+                         "plain copy kernel of known size that calibrates the rocprofv3 byte "
+                         "counters) and pure-read, pure-write and contiguous-copy kernels "
+                         "built like the library's")
     ap.add_argument("--copy-ceiling", action="store_true",
-                    help="also time torch copy_ of one 8 GiB buffer (a plain copy kernel of "
-                         "known size, used to calibrate the rocprofv3 byte counters)")
+                    help="time the torch copy_ reference even with --no-ceilings")
     ap.add_argument("--host-link-ceiling", action="store_true",
                     help="also time 4 GiB DMA copies between pinned host memory and HBM "
                          "(host-link reference rates)")
     ap.add_argument("--hbm-ceiling", action="store_true",
-                    help="also time pure-read, pure-write and contiguous-copy kernels built "
-                         "like the library's (HBM reference rates)")
+                    help="time the library-shaped read/write/copy references even with "
+                         "--no-ceilings")
     return ap
 
 
@@ -386,6 +429,18 @@ def main() -> int:
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = step_payload / (ms_per_step / 1e3) / 1e9
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} GB/s")
+    # per step, from the events on the stream: first call's start to last
+    # call's end (one stream; a duplex step spans two, so it has no median)
+    step_ms = None
+    if graph is not None:
+        step_ms = [evs[s][0][0].elapsed_time(evs[s][0][1]) for s in range(args.steps)]
+    elif not g.duplex:
+        step_ms = [evs[s][0][0].elapsed_time(evs[s][n_w - 1][1]) for s in range(args.steps)]
+    median_ms = None
+    if step_ms:
+        import statistics
+        median_ms = statistics.median(step_ms)
+        log(f"per-step median (events): {median_ms:.3f} ms")
 
     # per kernel (per graph replay with --graph), from the events around it
     kern = {}
@@ -442,13 +497,16 @@ def main() -> int:
                     "traffic": traffic}
 
     out = {
-        "metric": METRIC,
+        "metric": metric_for(cfg, info["block_size"], on_host),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": None if median_ms is None else round(median_ms, 4),
+        "value_at_median": None if median_ms is None else
+        round(step_payload / (median_ms / 1e3) / 1e9, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -473,7 +531,7 @@ def main() -> int:
         "cpu_baseline": None,
     }
 
-    if args.copy_ceiling:
+    if args.copy_ceiling or not args.no_ceilings:
         n = min(8 << 30, g.pool.numel() // 2)
         a, b = g.pool[:n], g.pool[n:2 * n]
         for _ in range(3):
@@ -497,7 +555,7 @@ def main() -> int:
         out["host_link_ceiling"] = host_link_ceiling(stream)
         log(f"host link reference rates: {out['host_link_ceiling']}")
 
-    if args.hbm_ceiling:
+    if args.hbm_ceiling or not args.no_ceilings:
         out["hbm_ceiling"] = hbm_ceiling(g.pool, stream)
         log(f"HBM reference rates: {out['hbm_ceiling']}")
 
@@ -510,6 +568,9 @@ def main() -> int:
         nt = cpu_threads()
         if nt > 1:
             out["cpu_baseline_threads"] = cpu_baseline(cfg, threads=nt)
+            out["cpu_baseline_threads"]["cores_note"] = (
+                f"{cpu_available()} CPUs available to the process; at most "
+                f"{HOST_SHARE_THREADS} used, one GPU's share of the host")
             log(f"cpu baseline, {nt} threads: {out['cpu_baseline_threads']['value']} GB/s")
     print(json.dumps(out), flush=True)
     return 0

@@ -65,3 +65,29 @@ def test_bench_refuses_more_than_one_gpu(argv, env):
     assert r.returncode == 2, r.stdout + r.stderr
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_metric_line_names_each_workload():
+    """The metric line names the workload's shapes and block size; for the
+    Kimi-Linear TP=1 workload it is the headline metric, word for word."""
+    headline = "store+retrieve GB/s of KV/state pages (Kimi-Linear shapes, N=1888); % HBM peak"
+    cfg = W.make_config("kl_tp1")
+    assert bench.metric_for(cfg, 1888, on_host=False) == headline
+    seen = set()
+    for name in W.CONFIG_NAMES + W.EXTRA_CONFIG_NAMES:
+        cfg = W.make_config(name)
+        lay = oracle.Layout(cfg.desc)
+        on_host = cfg.extra.get("objects") == "host"
+        m = bench.metric_for(cfg, lay.summary["block_size"], on_host)
+        assert f"N={lay.summary['block_size']}" in m
+        assert ("host-link" in m) == on_host
+        seen.add(m)
+    assert len(seen) == len(W.CONFIG_NAMES + W.EXTRA_CONFIG_NAMES)
+
+
+def test_ceiling_flags_parse():
+    ap = bench.build_parser()
+    a = ap.parse_args([])
+    assert not a.no_ceilings
+    a = ap.parse_args(["--no-ceilings", "--copy-ceiling"])
+    assert a.no_ceilings and a.copy_ceiling

@@ -242,6 +242,7 @@ class Config:
     shared_permutation: bool = False  # all phases draw ids from one permutation
     notes: str = ""
     extra: dict = field(default_factory=dict)
+    shapes: str = ""              # short name of the shapes, for the benchmark's metric line
 
 
 def _all_chunks(requests, first=None):
@@ -257,8 +258,30 @@ def _tiny_requests(seed: int) -> list:
     return [3 + s.next() % 3 for _ in range(4)]
 
 
+SHAPES = {
+    "tiny": "tiny 4-layer shapes",
+    "kl_tp2": "Kimi-Linear TP=2 rank shapes",
+    "kl_tp1": "Kimi-Linear shapes",
+    "k3_tp8": "K3-shaped TP=8 rank",
+    "long_ctx": "Kimi-Linear shapes, long context",
+    "kl_tp1_host": "Kimi-Linear shapes, pinned host objects",
+    "k3_tp8_holes": "K3-shaped TP=8 rank, KDA snapshots every 4th block",
+    "kl_tp1_tails": "Kimi-Linear shapes, partial tails",
+    "kl_tp1_host_duplex": "Kimi-Linear shapes, pinned host objects, store and retrieve at once",
+    "kl_tp1_int8": "Kimi-Linear shapes, INT8 KDA objects",
+    "kl_tp1_int8_host": "Kimi-Linear shapes, INT8 KDA objects in pinned host memory",
+}
+
+
 def make_config(name: str) -> Config:
-    """The five workloads at full size."""
+    """A workload at full size: the five of the benchmark's configurations
+    (CONFIG_NAMES) and the further ones (EXTRA_CONFIG_NAMES)."""
+    cfg = _make_config(name)
+    cfg.shapes = SHAPES[name]
+    return cfg
+
+
+def _make_config(name: str) -> Config:
     if name == "tiny":
         seed = 0x48B0001
         req = _tiny_requests(seed)
