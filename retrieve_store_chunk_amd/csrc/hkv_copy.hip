@@ -52,65 +52,31 @@ static __device__ __align__(256) uint8_t scratch[hkv::kStaticScratchBytes];
 
 namespace {
 
-// Build-time choices (defaults are the tuned ones).
-#ifndef HKV_STORE_UNROLL
-#define HKV_STORE_UNROLL 2     // gather: 16-byte loads per lane issued before their stores
-#endif
-#ifndef HKV_RETRIEVE_UNROLL
-#define HKV_RETRIEVE_UNROLL 1  // scatter: the same
-#endif
-#ifndef HKV_NT_LOAD
-#define HKV_NT_LOAD 1     // nontemporal loads
-#endif
-#ifndef HKV_NT_STORE
-#define HKV_NT_STORE 1    // nontemporal stores
-#endif
-#ifndef HKV_XCD_REMAP
-#define HKV_XCD_REMAP 1   // remap item order per XCD (hkv::xcd_first_item)
-#endif
-#ifndef HKV_STORE_XCD_RUN
-#define HKV_STORE_XCD_RUN 0        // gather: >0 = XCDs take turns on runs of this many items
-#endif
-#ifndef HKV_RETRIEVE_XCD_RUN
-#define HKV_RETRIEVE_XCD_RUN 8192  // scatter: the same
-#endif
-#ifndef HKV_CODEC_NT
-#define HKV_CODEC_NT 1    // nontemporal code / scale accesses in the codec
-#endif
-#ifndef HKV_GATHER_LDS
-#define HKV_GATHER_LDS 13312  // LDS bytes reserved per workgroup of the plain gather (occupancy cap)
-#endif
-#ifndef HKV_SCATTER_LDS
-#define HKV_SCATTER_LDS 12288  // the same for the plain scatter
-#endif
-#ifndef HKV_WAVES_PER_EU
-#define HKV_WAVES_PER_EU 0  // waves per SIMD the register budget must allow (0: any)
-#endif
-#if HKV_WAVES_PER_EU > 0
-#define HKV_OCCUPANCY __attribute__((amdgpu_waves_per_eu(HKV_WAVES_PER_EU)))
-#else
-#define HKV_OCCUPANCY
-#endif
-
 constexpr uint32_t kThreads = hkv::kCopyThreads;
 constexpr uint32_t kXcds = 8;  // MI355X: workgroups go round-robin over 8 XCDs
 
+// Per direction, as measured best on MI355X at the Kimi-Linear shapes:
+// 16-byte loads per lane issued before their stores; how the XCDs share the
+// items (0: each XCD one contiguous range; n: the XCDs take turns on runs of
+// n items); and the LDS each plain workgroup reserves without using it, which
+// caps a CU at 12 gather (160 KiB / 13 KiB) or 13 scatter workgroups.
+constexpr uint32_t kStoreUnroll = 2;
+constexpr uint32_t kRetrieveUnroll = 1;
+constexpr uint32_t kStoreXcdRun = 0;
+constexpr uint32_t kRetrieveXcdRun = 8192;
+constexpr uint32_t kGatherLds = 13312;
+constexpr uint32_t kScatterLds = 12288;
+
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
+// Every access is nontemporal: the pools are far larger than the caches and
+// nothing is read twice.
 __device__ __forceinline__ v4u load16(const HKV_GLOBAL v4u* p) {
-#if HKV_NT_LOAD
   return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
 }
 
 __device__ __forceinline__ void store16(HKV_GLOBAL v4u* p, v4u v) {
-#if HKV_NT_STORE
   __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
-#endif
 }
 
 // Copies `bytes` bytes from src to dst with all kThreads lanes of the
@@ -156,19 +122,11 @@ __device__ __forceinline__ void zero_span(uint8_t* dst, uint32_t bytes) {
 }
 
 __device__ __forceinline__ uint32_t load4(const HKV_GLOBAL uint32_t* p) {
-#if HKV_CODEC_NT
   return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
 }
 
 __device__ __forceinline__ void store4(HKV_GLOBAL uint32_t* p, uint32_t v) {
-#if HKV_CODEC_NT
   __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
-#endif
 }
 
 __device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -200,13 +158,19 @@ __device__ __forceinline__ float row_max(float m) {
   return m;
 }
 
-// INT8 codec of one group of recurrent-state rows (a KDA page under the
+// INT8 codec of one item's recurrent-state rows (a KDA page under the
 // codec: conv part, then fp32 rows of kD values).  kLanes lanes hold a row:
 // lane `sub` holds the row's 16-byte vectors sub, sub + kLanes, ... (so the
 // kLanes lanes of a row read 16 * kLanes contiguous bytes per load) and the
 // matching 4-code words.  All of a lane's loads are issued before any use.
 // Store: the row's largest finite |x| (DPP reduction), then 4 codes per
-// vector and, from lane 0, the row's scale.  Retrieve: q * s back.
+// vector; a lane computes all its code words before it stores any, so the
+// stores that fill one 128-byte line of codes leave back to back (a
+// nontemporal half-line followed much later by its other half makes the
+// line leave L2 in extra pieces: 2-5% more bytes written).  Lane 0 of the
+// row writes the row's scale with an ordinary store, so that the 4-byte
+// scales of neighbouring items merge in L2 into whole lines.
+// Retrieve: q * s back.
 // Quantisation (both sides of the parity tests take it in fp32, IEEE
 // division and round-half-even): s = max|x| / 127; q = rint(x / s) clamped
 // to [-127, 127]; 0 for non-finite x or s == 0 (Mooncake K3 blog, Compressed
@@ -234,13 +198,14 @@ __device__ __forceinline__ void codec_rows(const hkv::CopyArgs& a,
   }
   uint8_t* recurrent = a.pool + L->pool_offset + (uint64_t)id * L->stride + L->copy_bytes;
   for (uint32_t r = r0 + threadIdx.x / kLanes; r < r_end; r += kRowsPerPass) {
-    HKV_GLOBAL v4u* xp = (HKV_GLOBAL v4u*)(recurrent + (uint64_t)r * kD * 4) + sub;
-    HKV_GLOBAL uint32_t* qp = (HKV_GLOBAL uint32_t*)(codes + (uint64_t)r * kD) + sub;
-    HKV_GLOBAL float* sp = (HKV_GLOBAL float*)scales + r;
+    HKV_GLOBAL v4u* xp = (HKV_GLOBAL v4u*)(recurrent + (uint64_t)r * kD * 4);
+    HKV_GLOBAL uint32_t* qp = (HKV_GLOBAL uint32_t*)(codes + (uint64_t)r * kD);
+    HKV_GLOBAL uint32_t* sp = (HKV_GLOBAL uint32_t*)scales + r;
     if (kStore) {
       v4u raw[kVecs];
 #pragma unroll
-      for (uint32_t v = 0; v < kVecs; ++v) raw[v] = load16(xp + v * kLanes);
+      for (uint32_t v = 0; v < kVecs; ++v)
+        raw[v] = load16(xp + hkv::codec_input_vector(sub, v, kLanes));
       float m = 0.0f;
 #pragma unroll
       for (uint32_t v = 0; v < kVecs; ++v)
@@ -251,24 +216,28 @@ __device__ __forceinline__ void codec_rows(const hkv::CopyArgs& a,
         }
       m = row_max<kLanes>(m);
       const float scale = m / 127.0f;
+      uint32_t packed[kVecs];
 #pragma unroll
       for (uint32_t v = 0; v < kVecs; ++v) {
-        uint32_t packed = 0;
+        packed[v] = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float x = as_float(raw[v][i]);
           const float t = fminf(fmaxf(rintf(x / scale), -127.0f), 127.0f);
           const int q = (scale != 0.0f && __builtin_isfinite(x)) ? (int)t : 0;
-          packed |= ((uint32_t)q & 0xFFu) << (8 * i);
+          packed[v] |= ((uint32_t)q & 0xFFu) << (8 * i);
         }
-        store4(qp + v * kLanes, packed);
       }
-      if (sub == 0) store4((HKV_GLOBAL uint32_t*)sp, as_uint(scale));
+#pragma unroll
+      for (uint32_t v = 0; v < kVecs; ++v)
+        store4(qp + hkv::codec_input_vector(sub, v, kLanes), packed[v]);
+      if (sub == 0) *sp = as_uint(scale);
     } else {
       uint32_t packed[kVecs];
 #pragma unroll
-      for (uint32_t v = 0; v < kVecs; ++v) packed[v] = load4(qp + v * kLanes);
-      const float scale = as_float(load4((const HKV_GLOBAL uint32_t*)sp));
+      for (uint32_t v = 0; v < kVecs; ++v)
+        packed[v] = load4(qp + hkv::codec_input_vector(sub, v, kLanes));
+      const float scale = as_float(load4(sp));
 #pragma unroll
       for (uint32_t v = 0; v < kVecs; ++v) {
         v4u out;
@@ -276,7 +245,7 @@ __device__ __forceinline__ void codec_rows(const hkv::CopyArgs& a,
         out.y = decode_bits(packed[v] >> 8, scale);
         out.z = decode_bits(packed[v] >> 16, scale);
         out.w = decode_bits(packed[v] >> 24, scale);
-        store16(xp + v * kLanes, out);
+        store16(xp + hkv::codec_input_vector(sub, v, kLanes), out);
       }
     }
   }
@@ -303,43 +272,30 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a, const hkv::In
   const HKV_CONST int32_t* tokens = (const HKV_CONST int32_t*)(
       a.chunk_tokens ? a.chunk_tokens : reinterpret_cast<const int32_t*>(t.words + a.inline_tokens));
   const uint32_t total = (uint32_t)a.total_items;
-#if HKV_XCD_REMAP
   const uint32_t first = hkv::xcd_first_item(blockIdx.x, gridDim.x, kRun, kXcds);
-#else
-  const uint32_t first = blockIdx.x;
-#endif
   for (uint32_t item = first; item < total; item += gridDim.x) {
     const uint32_t c = item / a.items_per_chunk;
-    const uint32_t r = item - c * a.items_per_chunk;
-    const uint64_t w = items[r];
-    const uint32_t l = (uint32_t)(w & 0xFFFFu);
-    const uint32_t j = (uint32_t)((w >> 16) & 0xFFFFu);
-    const uint32_t s = (uint32_t)((w >> 32) & 0x7FFFFFFFu);
-    const HKV_CONST hkv::DevLayer* L = layers + l;
+    const uint64_t w = items[item - c * a.items_per_chunk];
+    const uint32_t j = hkv::item_block(w);
+    const HKV_CONST hkv::DevLayer* L = layers + hkv::item_layer(w);
     const int32_t id = ids[((uint64_t)c * a.n_kv_groups + L->kv_group) * a.blocks_per_chunk + j];
     uint8_t* obj = reinterpret_cast<uint8_t*>(objs[(uint64_t)c * a.n_obj_groups + L->obj_group]);
     uint8_t* obj_page = obj + L->obj_offset + (uint64_t)j * L->obj_page;
-    if (w >> 63) {  // a codec row group of a KDA page (INT8 layouts only)
-      if constexpr (kD != 0) codec_rows<kD, kStore>(a, L, id, obj_page, s);
+    if (hkv::item_kind(w)) {  // a codec row group of a KDA page (INT8 layouts only)
+      if constexpr (kD != 0) codec_rows<kD, kStore>(a, L, id, obj_page, hkv::item_index(w));
       continue;
     }
-    const uint64_t span = L->copy_bytes;  // the page, or the conv part under the codec
-    const uint64_t off = (uint64_t)s * a.tile_bytes;
-    const uint64_t rest = span - off;
-    const uint32_t bytes = (uint32_t)(rest < a.tile_bytes ? rest : a.tile_bytes);
-    uint8_t* obj_tile = obj_page + off;
-    // Bytes of this span that hold data: all of it, none for a null id, and
-    // for an MLA page of a partial chunk the rows of its valid tokens.
-    uint64_t valid = id < 0 ? 0 : span;
-    if (a.has_tokens && L->row_bytes && id >= 0) {
-      int64_t rows = (int64_t)tokens[c] - (int64_t)j * (int64_t)a.block_tokens;
-      rows = rows < 0 ? 0 : (rows > (int64_t)a.block_tokens ? (int64_t)a.block_tokens : rows);
-      valid = (uint64_t)rows * L->row_bytes;
-    }
-    const uint32_t live =
-        valid > off ? (uint32_t)(valid - off < bytes ? valid - off : bytes) : 0u;
+    // the page (or the conv part under the codec): this tile's bytes, and
+    // those of them that hold data
+    const uint64_t span = L->copy_bytes;
+    const hkv::TileSpan ts = hkv::tile_span(
+        span, hkv::item_index(w), a.tile_bytes,
+        hkv::live_span_bytes(id, span, L->row_bytes, a.has_tokens != 0,
+                             a.has_tokens ? (int64_t)tokens[c] : 0, j, a.block_tokens));
+    const uint32_t bytes = ts.bytes, live = ts.live;
+    uint8_t* obj_tile = obj_page + ts.off;
     if (live) {
-      uint8_t* page = a.pool + L->pool_offset + (uint64_t)id * L->stride + off;
+      uint8_t* page = a.pool + L->pool_offset + (uint64_t)id * L->stride + ts.off;
       if (kStore)
         copy_span<kUnroll>(obj_tile, page, live);
       else
@@ -354,13 +310,13 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a, const hkv::In
 // The gather (store) and scatter (retrieve) kernels: one pair for layouts
 // without the codec, and one pair per head_dim for INT8 layouts.
 #define HKV_KERNEL_PAIR(suffix, kD)                                            \
-  extern "C" __global__ __launch_bounds__(kThreads) HKV_OCCUPANCY void         \
+  extern "C" __global__ __launch_bounds__(kThreads) void                       \
       hkv_store_gather##suffix(hkv::CopyArgs a, hkv::InlineTables t) {         \
-    copy_items<true, HKV_STORE_UNROLL, HKV_STORE_XCD_RUN, kD>(a, t);           \
+    copy_items<true, kStoreUnroll, kStoreXcdRun, kD>(a, t);                    \
   }                                                                            \
-  extern "C" __global__ __launch_bounds__(kThreads) HKV_OCCUPANCY void         \
+  extern "C" __global__ __launch_bounds__(kThreads) void                       \
       hkv_retrieve_scatter##suffix(hkv::CopyArgs a, hkv::InlineTables t) {     \
-    copy_items<false, HKV_RETRIEVE_UNROLL, HKV_RETRIEVE_XCD_RUN, kD>(a, t);    \
+    copy_items<false, kRetrieveUnroll, kRetrieveXcdRun, kD>(a, t);             \
   }
 
 HKV_KERNEL_PAIR(, 0)
@@ -421,7 +377,7 @@ int launch_copy(bool store, const CopyArgs& a, const InlineTables& t, uint32_t g
   // The plain kernels need few registers and would run 8 waves per SIMD; they
   // measured best with fewer.  Reserving LDS they do not use caps a CU at 12
   // gather workgroups (160 KiB / 13 KiB) or 13 scatter workgroups (12 KiB).
-  const uint32_t lds = a.codec_head_dim != 0 ? 0u : store ? HKV_GATHER_LDS : HKV_SCATTER_LDS;
+  const uint32_t lds = a.codec_head_dim != 0 ? 0u : store ? kGatherLds : kScatterLds;
   return (int)hipLaunchKernel(fn, dim3(grid), dim3(kThreads), params, lds,
                               reinterpret_cast<hipStream_t>(stream));
 }

@@ -32,23 +32,64 @@ inline constexpr uint64_t pack_item(uint32_t layer, uint32_t j, uint32_t index, 
   return (uint64_t)(layer & 0xFFFFu) | ((uint64_t)(j & 0xFFFFu) << 16) |
          ((uint64_t)(index & 0x7FFFFFFFu) << 32) | ((uint64_t)(kind & 1u) << 63);
 }
+inline constexpr uint32_t item_layer(uint64_t w) { return (uint32_t)(w & 0xFFFFu); }
+inline constexpr uint32_t item_block(uint64_t w) { return (uint32_t)((w >> 16) & 0xFFFFu); }
+inline constexpr uint32_t item_index(uint64_t w) { return (uint32_t)((w >> 32) & 0x7FFFFFFFu); }
+inline constexpr uint32_t item_kind(uint64_t w) { return (uint32_t)(w >> 63); }
 
-#ifndef HKV_CODEC_VECS
-#define HKV_CODEC_VECS 2  // most 16-byte vectors a lane holds of a codec row (1..8)
-#endif
-static_assert(HKV_CODEC_VECS == 1 || HKV_CODEC_VECS == 2 || HKV_CODEC_VECS == 4 ||
-                  HKV_CODEC_VECS == 8,
-              "HKV_CODEC_VECS");
+// The following are the per-item arithmetic of the copy kernels, shared with
+// the host programs that replay it (constexpr functions compile for both).
+
+// Bytes at the start of a verbatim span (a page, or the conv part of a codec
+// page) that hold data: all `span` bytes, none for a null id (id < 0), and
+// for an MLA page (row_bytes > 0) of a partial chunk with `tokens` valid
+// tokens, the rows [j * block_tokens, tokens) that fall into block j.
+inline constexpr uint64_t live_span_bytes(int32_t id, uint64_t span, uint32_t row_bytes,
+                                          bool has_tokens, int64_t tokens, uint32_t j,
+                                          uint64_t block_tokens) {
+  if (id < 0) return 0;
+  if (!has_tokens || row_bytes == 0) return span;
+  int64_t rows = tokens - (int64_t)j * (int64_t)block_tokens;
+  rows = rows < 0 ? 0 : (rows > (int64_t)block_tokens ? (int64_t)block_tokens : rows);
+  return (uint64_t)rows * row_bytes;
+}
+
+// Tile s of a span: its offset, its length (tile_bytes, the last one
+// shorter) and how many of its bytes hold data (`valid` from
+// live_span_bytes); a store zero-fills the rest of the tile in the object.
+struct TileSpan {
+  uint64_t off;
+  uint32_t bytes;
+  uint32_t live;
+};
+inline constexpr TileSpan tile_span(uint64_t span, uint32_t s, uint64_t tile_bytes,
+                                    uint64_t valid) {
+  const uint64_t off = (uint64_t)s * tile_bytes;
+  const uint64_t rest = span - off;
+  const uint32_t bytes = (uint32_t)(rest < tile_bytes ? rest : tile_bytes);
+  const uint32_t live = valid > off ? (uint32_t)(valid - off < bytes ? valid - off : bytes) : 0u;
+  return TileSpan{off, bytes, live};
+}
+
+// Most 16-byte vectors a lane holds of a codec row.
+constexpr uint32_t kCodecVecs = 2;
 
 // Lanes that hold one recurrent-state row of head_dim fp32 values in a codec
-// item: head_dim / (4 * HKV_CODEC_VECS), kept within 4..16 (a row's lanes
-// reduce with DPP inside one row of 16 lanes), so each lane holds
+// item: head_dim / (4 * kCodecVecs), kept within 4..16 (a row's lanes reduce
+// with DPP inside one row of 16 lanes), so each lane holds
 // head_dim / (4 * lanes) 16-byte vectors.  A workgroup of `threads` lanes
 // takes threads / lanes rows a pass.
 inline constexpr uint32_t codec_lanes_per_row(uint32_t head_dim) {
-  return head_dim / (4 * HKV_CODEC_VECS) < 4    ? 4
-         : head_dim / (4 * HKV_CODEC_VECS) > 16 ? 16
-                                                : head_dim / (4 * HKV_CODEC_VECS);
+  return head_dim / (4 * kCodecVecs) < 4    ? 4
+         : head_dim / (4 * kCodecVecs) > 16 ? 16
+                                            : head_dim / (4 * kCodecVecs);
+}
+
+// In a codec row, lane `sub`'s v-th 16-byte vector of fp32 input (so the
+// row's lanes read contiguous bytes per load); its 4 codes are the row's
+// 4-byte code word of the same index.
+inline constexpr uint32_t codec_input_vector(uint32_t sub, uint32_t v, uint32_t lanes) {
+  return sub + v * lanes;
 }
 
 // The work item that workgroup b of a grid of `grid` workgroups takes first

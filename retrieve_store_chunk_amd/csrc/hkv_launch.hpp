@@ -7,10 +7,7 @@
 
 namespace hkv {
 
-#ifndef HKV_THREADS
-#define HKV_THREADS 128  // two waves per workgroup
-#endif
-constexpr uint32_t kCopyThreads = HKV_THREADS;
+constexpr uint32_t kCopyThreads = 128;  // two waves per workgroup
 
 // Enqueues the gather (store) or scatter (retrieve) kernel over
 // a.total_items work items with `grid` workgroups on `stream` (a

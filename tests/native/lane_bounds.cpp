@@ -1,9 +1,11 @@
 // The copy kernels' index arithmetic replayed on the host over real plan
-// tables: for every work item of a call, every lane's loads and stores
-// (16-byte copy vectors, or a codec item's 16-byte row loads, 4-byte code
-// words and row scale) stay inside their page, row and object, are aligned
-// for their width, and every object byte is written exactly once.  The DPP
-// partners of the codec's row reduction stay inside the row's lanes.
+// tables, through the same helpers the kernels call (item decode, live
+// bytes, tile spans, codec lane map in hkv_device_tables.hpp): for every
+// work item of a call, every lane's loads and stores (16-byte copy vectors,
+// or a codec item's 16-byte row loads, 4-byte code words and row scale) stay
+// inside their page, row and object, are aligned for their width, and every
+// object byte is written exactly once.  The DPP partners of the codec's row
+// reduction stay inside the row's lanes.
 // Layouts: the five workloads' shapes and small ones with head_dim 16..256,
 // three tile sizes, with and without the INT8 codec, with and without null
 // ids and partial chunks.
@@ -46,7 +48,8 @@ int check(const char* name, std::vector<uint8_t> is_mla, int heads, int d, int c
   };
   for (uint64_t item=0; item<total; item++) {
     uint32_t c = item/ipc, r = item - c*ipc; uint64_t w = p.items[r];
-    uint32_t l = w & 0xFFFF, j = (w>>16)&0xFFFF, s = (w>>32) & 0x7FFFFFFF, kind = w >> 63;
+    const uint32_t l = hkv::item_layer(w), j = hkv::item_block(w), s = hkv::item_index(w);
+    const uint32_t kind = hkv::item_kind(w);
     if (l >= p.dev_layers.size() || j >= k) FAIL("bad item");
     const hkv::DevLayer& L = p.dev_layers[l];
     int32_t id = ids[((uint64_t)c*G + L.kv_group)*k + j];
@@ -61,8 +64,8 @@ int check(const char* name, std::vector<uint8_t> is_mla, int heads, int d, int c
       if ((lpr != 4 && lpr != 8 && lpr != 16) || kThreads % lpr || dd % (4 * lpr)) FAIL("lanes per row %u", lpr);
       const uint32_t vecs = dd / (4 * lpr);
       if (vecs > 8) FAIL("vectors per lane %u", vecs);
-      const uint32_t rpi = kThreads / lpr;
-      if (p.codec_rows_per_item % rpi) FAIL("rows per item not whole passes");
+      const uint32_t rpp = kThreads / lpr;     // rows per pass
+      if (p.codec_rows_per_item % rpp) FAIL("rows per item not whole passes");
       const uint32_t r0 = s * p.codec_rows_per_item;
       const uint32_t r_end = std::min<uint32_t>(r0 + p.codec_rows_per_item, rows);
       if (r0 >= rows) FAIL("codec group past rows");
@@ -81,14 +84,15 @@ int check(const char* name, std::vector<uint8_t> is_mla, int heads, int d, int c
         if ((t ^ 1u) / lpr != t / lpr || (t ^ 2u) / lpr != t / lpr) FAIL("quad swap leaves the row");
         if (lpr >= 8 && ((t & ~7u) | (7u - (t & 7u))) / lpr != t / lpr) FAIL("half mirror leaves the row");
         if (lpr >= 16 && ((t & ~15u) | (15u - (t & 15u))) / lpr != t / lpr) FAIL("mirror leaves the row");
-        for (uint32_t rr = r0 + t/lpr; rr < r_end; rr += rpi) {
+        for (uint32_t rr = r0 + t/lpr; rr < r_end; rr += rpp) {
           for (uint32_t v = 0; v < vecs; v++) {
-            const uint64_t x = rec + (uint64_t)rr*dd*4 + (uint64_t)(v*lpr + sub)*16;
+            const uint32_t vi = hkv::codec_input_vector(sub, v, lpr);
+            const uint64_t x = rec + (uint64_t)rr*dd*4 + (uint64_t)vi*16;
             if (x % 16) FAIL("unaligned 16-B load");
             if (x < rec + (uint64_t)rr*dd*4 || x + 16 > rec + (uint64_t)(rr+1)*dd*4) FAIL("load leaves its row");
             if (x + 16 > L.pool_offset + (uint64_t)id*L.stride + L.page || x + 16 > p.pool_used) FAIL("load past page");
             // the 4 codes of that vector: one 4-byte word of the row's codes
-            const uint64_t q = codes + (uint64_t)rr*dd + (uint64_t)(v*lpr + sub)*4;
+            const uint64_t q = codes + (uint64_t)rr*dd + (uint64_t)vi*4;
             if (q % 4) FAIL("unaligned code store");
             if (q < codes + (uint64_t)rr*dd || q + 4 > codes + (uint64_t)(rr+1)*dd) FAIL("code store leaves its row");
             if (int e = mark(cv, q, 4)) FAIL("code store %s", e==1?"overflow":"twice");
@@ -99,13 +103,11 @@ int check(const char* name, std::vector<uint8_t> is_mla, int heads, int d, int c
       }
       continue;
     }
-    uint64_t span = L.copy_bytes;
-    uint64_t off = (uint64_t)s*p.tile_bytes;
-    if (off >= span) FAIL("tile past span");
-    uint64_t rest = span - off, bytes = rest < p.tile_bytes ? rest : p.tile_bytes;
-    uint64_t valid = id < 0 ? 0 : span;
-    if (L.row_bytes && id >= 0) { int64_t rows = (int64_t)toks[c] - (int64_t)j * p.block_size; rows = rows < 0 ? 0 : (rows > p.block_size ? p.block_size : rows); valid = rows * L.row_bytes; }
-    uint64_t live = valid > off ? (valid - off < bytes ? valid - off : bytes) : 0;
+    const uint64_t span = L.copy_bytes;
+    if ((uint64_t)s*p.tile_bytes >= span) FAIL("tile past span");
+    const hkv::TileSpan ts = hkv::tile_span(span, s, p.tile_bytes,
+        hkv::live_span_bytes(id, span, L.row_bytes, nulls, toks[c], j, (uint64_t)p.block_size));
+    const uint64_t off = ts.off, bytes = ts.bytes, live = ts.live;
     if (live) {
       if (id < 0) FAIL("live bytes for a null id");
       uint64_t src = L.pool_offset + (uint64_t)id*L.stride + off;
