@@ -16,7 +16,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libhkvref.so")
+DEFAULT_LIB_PATH = os.path.join(HERE, "libhkvref.so")
+# HKVREF_LIB names another build of hkvref.c (the tests' sanitized build).
+LIB_PATH = os.environ.get("HKVREF_LIB") or DEFAULT_LIB_PATH
 
 DESC_KEYS = (
     "is_mla", "kda_heads", "kda_head_dim", "kda_state_bytes", "conv_dim", "conv_kernel",
@@ -40,7 +42,7 @@ class OracleError(RuntimeError):
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
+        if not os.path.exists(LIB_PATH) and LIB_PATH == DEFAULT_LIB_PATH:
             from . import build as _build  # noqa: F401  (build on first use)
             _build.build()
         _lib = bind(ctypes.CDLL(LIB_PATH))

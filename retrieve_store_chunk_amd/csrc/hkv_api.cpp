@@ -286,7 +286,7 @@ hkv_status stream_state(void* stream, int* dev, bool* capturing) {
 }
 
 // ---------------------------------------------------------------- layout tables
-constexpr uint64_t layer_table_bytes(const hkv::Plan& p) {
+uint64_t layer_table_bytes(const hkv::Plan& p) {
   return hkv::align256(p.dev_layers.size() * sizeof(hkv::DevLayer));
 }
 

@@ -82,7 +82,10 @@ void fill_grouped_tables(const Plan& p, const hkv_chunk_batch& b, const GroupedC
   uint64_t* ob = reinterpret_cast<uint64_t*>(h + g.ws.objs_off);
   int32_t* tk = reinterpret_cast<int32_t*>(h + g.ws.tokens_off);
   for (size_t c = 0; c < g.members.size(); ++c) {
-    std::memcpy(it, g.items[c].data(), g.items[c].size() * sizeof(uint64_t));
+    // (a class may have no items: memcpy from an empty vector's null data
+    // pointer is undefined even for zero bytes)
+    if (!g.items[c].empty())
+      std::memcpy(it, g.items[c].data(), g.items[c].size() * sizeof(uint64_t));
     it += g.items[c].size();
     for (const uint32_t ch : g.members[c]) {
       std::memcpy(id, b.block_ids + (uint64_t)ch * G * k, G * k * sizeof(int32_t));
