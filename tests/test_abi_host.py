@@ -396,3 +396,21 @@ def test_error_messages_are_per_thread():
     for th in threads:
         th.join()
     assert not failures, failures[:4]
+
+
+def test_trace_names_the_block_size():
+    """HKV_TRACE=1: the layout's block size and chunk size on stderr, like
+    the engine's own line naming the block size it settled on."""
+    import subprocess
+    import sys
+    code = ("import workloads, retrieve_store_chunk_amd as hkv; "
+            "hkv.Layout(workloads.make_config('kl_tp1').desc); "
+            "hkv.Layout(workloads.make_config('k3_tp8').desc)")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       timeout=300, cwd=ROOT, env=dict(os.environ, HKV_TRACE="1"))
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "block size N=1888 tokens, chunk C=1888 (k=1), path B" in r.stderr
+    assert "block size N=768 tokens, chunk C=1536 (k=2), path A" in r.stderr
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       timeout=300, cwd=ROOT, env=dict(os.environ, HKV_TRACE="0"))
+    assert "[hkv]" not in r.stderr

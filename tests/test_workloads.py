@@ -45,11 +45,12 @@ def test_wave_plans_fit_the_pool(name, small):
     cfg = W.make_small_config(name) if small else W.make_config(name)
     lay = oracle.Layout(cfg.desc)
     s = lay.summary
-    waves = W.plan_waves(cfg, s["num_blocks"], lay.G, lay.k)
+    waves = _plan(cfg, lay)
     seen_store = set()
     for wv in waves:
         assert wv.ids.shape == (len(wv.chunks), lay.G, lay.k)
         flat = wv.ids.reshape(-1)
+        flat = flat[flat != W.NULL_BLOCK]  # tails: no KDA snapshot for an incomplete block
         assert flat.min() >= 0 and flat.max() < s["num_blocks"]
         assert len(set(flat.tolist())) == flat.size  # unique within a wave
         reqs = sorted({r for r, _ in wv.chunks})
@@ -65,7 +66,29 @@ def test_wave_plans_fit_the_pool(name, small):
             assert set(ph.chunks) <= seen_store
     if cfg.shared_permutation:
         allids = np.concatenate([wv.ids.reshape(-1) for wv in waves])
+        allids = allids[allids != W.NULL_BLOCK]
         assert len(set(allids.tolist())) == allids.size
+
+
+def _plan(cfg, lay):
+    s = lay.summary
+    kda = {L["kv_group"] for L in lay.layers if not L["is_mla"]}
+    return W.plan_waves(cfg, s["num_blocks"], lay.G, lay.k, kda, s["block_size"],
+                        s["chunk_tokens"])
+
+
+def test_long_context_prefix_and_tails():
+    """1,000,000 tokens are 529 whole chunks of 1888 and a 1,248-token one;
+    a 2,048-token request is one whole chunk and a 160-token tail."""
+    cfg = W.make_config("long_ctx")
+    lay = oracle.Layout(cfg.desc)
+    ret, st = _plan(cfg, lay)
+    assert ret.op == "retrieve" and len(ret.chunks) == 530
+    assert int(ret.chunk_tokens.sum()) == 1_000_000
+    assert st.op == "store" and len(st.chunks) == 1024
+    assert int(st.chunk_tokens.sum()) == 512 * 2048
+    kda = [L["kv_group"] for L in lay.layers if not L["is_mla"]]
+    assert (ret.ids[-1, sorted(set(kda)), :] == W.NULL_BLOCK).all()
 
 
 def test_full_config_wave_counts():
@@ -73,7 +96,7 @@ def test_full_config_wave_counts():
     for name, (ns, nr) in expect.items():
         cfg = W.make_config(name)
         lay = oracle.Layout(cfg.desc)
-        waves = W.plan_waves(cfg, lay.summary["num_blocks"], lay.G, lay.k)
+        waves = _plan(cfg, lay)
         assert sum(w.op == "store" for w in waves) == ns
         assert sum(w.op == "retrieve" for w in waves) == nr
     cfg = W.make_config("k3_tp8")

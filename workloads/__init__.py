@@ -317,15 +317,25 @@ def _make_config(name: str) -> Config:
                       seed)
     if name == "long_ctx":
         seed = 0x48B0005
-        req = [530] + [1] * 512
+        # 1,000,000 tokens = 529 whole chunks of 1888 + a 1,248-token partial
+        # one; a 2,048-token request = one whole chunk + a 160-token tail
+        prefix_tokens, request_tokens, chunk = 1_000_000, 2048, 1888
+        n_prefix = -(-prefix_tokens // chunk)
+        req = [n_prefix] + [2] * 512
         desc = _desc(KIMI_LINEAR_27, 32, 128, 12288, 2, 1, 100 * GIB)
-        return Config(name, "Long context: 530-chunk prefix retrieve + 512 tail stores, "
-                      "path B, 100 GiB pool", desc, req,
-                      [Phase("retrieve", [(0, c) for c in range(530)], prefilled_objects=True),
-                       Phase("store", [(r, 0) for r in range(1, 513)])],
+        prefix_tail = {(0, n_prefix - 1): prefix_tokens - (n_prefix - 1) * chunk}
+        tails = {(r, 1): request_tokens - chunk for r in range(1, 513)}
+        return Config(name, "Long context: 1,000,000-token prefix retrieve (529 whole chunks "
+                      "+ a 1,248-token tail) + 512 stores of 2,048-token requests, path B, "
+                      "100 GiB pool", desc, req,
+                      [Phase("retrieve", [(0, c) for c in range(n_prefix)],
+                             prefilled_objects=True, tail_tokens=prefix_tail),
+                       Phase("store", [(r, c) for r in range(1, 513) for c in range(2)],
+                             tail_tokens=tails)],
                       seed, shared_permutation=True,
-                      notes="a 1,000,000-token prefix is 530 whole chunks of 1888 tokens; each "
-                            "2k-token request has one whole chunk")
+                      notes="the prefix is 529 whole chunks of 1888 tokens and a last chunk of "
+                            "1,248 tokens (MLA rows only: its KDA block is not complete); each "
+                            "2,048-token request stores one whole chunk and a 160-token tail")
     if name == "kl_tp1_host":
         seed = 0x48B0006
         req = [8] * 16
@@ -459,9 +469,11 @@ def make_small_config(name: str) -> Config:
                       Phase("retrieve", _all_chunks(cfg.requests), tail_tokens=tails)]
     elif name == "long_ctx":
         cfg.desc["pool_bytes"] = 1 * GIB
-        cfg.requests = [8] + [1] * 8
-        cfg.phases = [Phase("retrieve", [(0, c) for c in range(8)], prefilled_objects=True),
-                      Phase("store", [(r, 0) for r in range(1, 9)])]
+        cfg.requests = [6] + [2] * 4
+        cfg.phases = [Phase("retrieve", [(0, c) for c in range(6)], prefilled_objects=True,
+                            tail_tokens={(0, 5): 1248}),
+                      Phase("store", [(r, c) for r in range(1, 5) for c in range(2)],
+                            tail_tokens={(r, 1): 160 for r in range(1, 5)})]
     cfg.name = name + "_small"
     return cfg
 
