@@ -1,8 +1,7 @@
 """The committed rocprofv3 summaries (no GPU): every command in them runs a
 committed program that the profiler starts directly, with flags the
 benchmark accepts, and every stored traffic figure matches the algorithmic
-bytes of the launches it was taken on (within 0.1%, except the INT8
-gather's writes)."""
+bytes of the launches it was taken on (within 0.1%)."""
 import glob
 import json
 import os
@@ -79,10 +78,7 @@ def test_traffic_figures_match_the_algorithmic_bytes(path):
     assert got == t[kern + "_bytes_per_launch"]
     assert got == pytest.approx(t[kern + "_read_bytes"] + t[kern + "_write_bytes"], abs=2)
     assert abs(t[kern + "_read_bytes"] / alg_read - 1) < 1e-3
-    # The INT8 gather's nontemporal stores of 4-byte codes and row scales
-    # write 3.2% more than the objects hold (partial lines written back
-    # separately); every other launch writes its algorithmic bytes.
-    write_tol = 0.05 if cfg.desc.get("kda_codec") else 1e-3
-    assert abs(t[kern + "_write_bytes"] / alg_write - 1) < write_tol
-    assert abs(got / (alg_read + alg_write) - 1) < write_tol
+    # every launch, the INT8 gather's included, writes its algorithmic bytes
+    assert abs(t[kern + "_write_bytes"] / alg_write - 1) < 1e-3
+    assert abs(got / (alg_read + alg_write) - 1) < 1e-3
     assert len(t["kernel_sha"]) == 16
