@@ -306,6 +306,11 @@ def build_parser() -> argparse.ArgumentParser:
                          "(default: the workload's choice, else the kernel)")
     ap.add_argument("--max-workgroups", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--entry", choices=("workspace", "noalloc"), default="workspace",
+                    help="the calls timed: hkv_store_chunks / hkv_retrieve_chunks with a "
+                         "workspace (default), or hkv_move_chunks_noalloc (kernel engine; a "
+                         "call whose tables exceed one launch's kernel arguments is split "
+                         "into several launches, timed together)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step's calls into a HIP graph after the warm-up and "
                          "time its replays (every call's tables must fit in its kernel "
@@ -346,8 +351,15 @@ def main() -> int:
     cfg = W.make_config(args.config)
     log(f"workload {cfg.name}: {cfg.title}")
     objects_on = cfg.extra.get("objects", "device")
+    if args.entry == "noalloc" and args.retrieve_engine == "dma":
+        print("--entry noalloc runs the kernel engine only", file=sys.stderr)
+        return 2
     g = GpuWorkload(cfg, tile_bytes=args.tile_bytes, max_workgroups=args.max_workgroups,
-                    objects=objects_on, retrieve_engine=args.retrieve_engine)
+                    objects=objects_on, retrieve_engine=args.retrieve_engine, entry=args.entry)
+    if args.entry == "noalloc" and g.retrieve_engine:
+        print(f"--entry noalloc runs the kernel engine only; {cfg.name} retrieves by DMA",
+              file=sys.stderr)
+        return 2
     info = g.info
     log(f"layout: N={info['block_size']} C={info['chunk_tokens']} k={info['blocks_per_chunk']} "
         f"blocks={info['num_blocks']} stride={info['block_stride']} "
@@ -490,12 +502,16 @@ def main() -> int:
                     "frac": round(achieved / HOST_LINK_PEAK_GBS, 4), "traffic": None}
     else:
         achieved = kernels[dom]["hbm_GBs"]
+        # the stored counters were taken on the workspace entry points' launches
         traffic = load_traffic(args.config, args.tile_bytes, args.max_workgroups) \
-            if dom.startswith("hkv_store_gather") else None
+            if dom.startswith("hkv_store_gather") and args.entry == "workspace" else None
         roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic}
 
+    if args.entry == "noalloc":
+        # a no-allocation call may be several launches; its events span them all
+        roofline["timed"] = "per call"
     out = {
         "metric": metric_for(cfg, info["block_size"], on_host),
         "value": round(value, 2),
@@ -520,7 +536,7 @@ def main() -> int:
                    "path": "B packed" if info["path"] else "A padded-unified",
                    "tile_bytes": args.tile_bytes, "max_workgroups": args.max_workgroups,
                    "retrieve_engine": "dma" if g.retrieve_engine else "kernel",
-                   "graph": graph is not None},
+                   "graph": graph is not None, "entry": args.entry},
         "objects": objects_on,
         "pct_hbm_peak": None if on_host else
         round(100 * step_hbm / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 2),

@@ -35,12 +35,15 @@ def _log(msg):
 FULL_SIZE = list(W.CONFIG_NAMES + W.EXTRA_CONFIG_NAMES)
 
 
-@pytest.mark.parametrize("name", FULL_SIZE)
-def test_full_size_every_byte(name):
+def run_every_byte(name, entry="workspace"):
+    """One full-size workload through the given entry point ("workspace":
+    hkv_store_chunks / hkv_retrieve_chunks; "noalloc": hkv_move_chunks_noalloc),
+    every pool byte checked after every wave and every object byte."""
     from workloads.runner import GpuWorkload
     cfg = W.make_config(name)
-    _log(f"[fullsize] {name}")
-    g = GpuWorkload(cfg, objects=cfg.extra.get("objects", "device"))
+    tag = f"[fullsize] {name}" + ("" if entry == "workspace" else f" ({entry})")
+    _log(tag)
+    g = GpuWorkload(cfg, objects=cfg.extra.get("objects", "device"), entry=entry)
     chk = Checker(cfg, g, DeviceBuild())
     g.init_pool()
     obj_seed = W.derive_seed(cfg.seed, 77)
@@ -52,7 +55,7 @@ def test_full_size_every_byte(name):
 
     def on_wave(i, w):
         chk.on_wave(i, w)
-        _log(f"[fullsize] {name}: wave {i} ({w.op}, {len(w.chunks)} chunks) matches")
+        _log(f"{tag}: wave {i} ({w.op}, {len(w.chunks)} chunks) matches")
 
     g.run_all(on_wave=on_wave)
     g.synchronize()
@@ -61,10 +64,15 @@ def test_full_size_every_byte(name):
     pool_total = g.pool.numel()
     obj_total = sum(g.objs[o].numel() for o in range(chk.ref.O))
     assert s["pool_bytes"] == s["waves"] * pool_total
-    _log(f"[fullsize] {name}: {s['waves']} waves; every pool byte compared after every wave "
+    _log(f"{tag}: {s['waves']} waves; every pool byte compared after every wave "
          f"({pool_total / 1e9:.1f} GB each), {s['obj_bytes'] / 1e9:.1f} GB of object bytes "
          f"compared (all {obj_total / 1e9:.1f} GB at the end), {s['codec_pages']} INT8 pages "
          f"against the oracle's codec")
     chk.pool_exec.shutdown()
     del g
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", FULL_SIZE)
+def test_full_size_every_byte(name):
+    run_every_byte(name)

@@ -7,7 +7,9 @@ smaller, then two retrieves in a row, the second smaller.  The cases cover
 calls that need several launches (more chunks than one launch's kernel
 arguments hold), null ids and partial chunks, the INT8 codec, and layouts
 that take turns on the static scratch (its tables are copied in again).
-The tiny workload is also checked against the oracle.
+The tiny workload is also checked against the oracle, full-size workloads
+run through the no-allocation entry point with every byte checked, and
+captured no-allocation calls replay correctly.
 """
 import numpy as np
 import pytest
@@ -217,3 +219,71 @@ def test_noalloc_oracle_round_trip_tiny():
     for c in range(n):
         for o in range(ref.O):
             assert np.array_equal(objs[c][o].cpu().numpy(), objs_ref[c][o])
+
+
+# Full-size workloads through the no-allocation entry point alone, in the
+# launch configuration the benchmark times: every pool byte after every wave
+# and every object byte against the bytes rebuilt from the oracle's
+# placements (the checker of the full-size parity tests).
+NOALLOC_FULL_SIZE = ["kl_tp1", "k3_tp8_holes", "long_ctx", "kl_tp1_int8"]
+
+
+@pytest.mark.parametrize("name", NOALLOC_FULL_SIZE)
+def test_noalloc_full_size_every_byte(name):
+    from tests.test_gpu_fullsize import run_every_byte
+    run_every_byte(name, entry="noalloc")
+
+
+@pytest.mark.parametrize("name", ["tiny", "kl_tp1", "k3_tp8_holes"])
+def test_noalloc_graph_capture_replays(name):
+    """A no-allocation store and retrieve captured into one HIP graph, after
+    one eager call has put the layout's tables in the static scratch.  Three
+    replays, with new pool and object bytes written eagerly before each, all
+    match the oracle applied to that replay's inputs."""
+    import retrieve_store_chunk_amd as hkv
+    from workloads.runner import GpuWorkload
+    cfg = W.make_config(name) if name == "tiny" else W.make_small_config(name)
+    _log(f"[noalloc graph] {name}")
+    g = GpuWorkload(cfg, entry="noalloc")
+    ref = oracle.Layout(cfg.desc)
+    calls = []
+    for op in ("store", "retrieve"):
+        w = next(w for w in g.waves if w.op == op)
+        tok = None if w.chunk_tokens is None else w.chunk_tokens[:8].copy()
+        calls.append((w.chunks[:8], w.ids[:8].copy(), tok))
+    (s_chunks, s_ids, s_tok), (r_chunks, r_ids, r_tok) = calls
+    P, S = g.pool.data_ptr(), g.stream
+    g.init_pool()
+    g.layout.move_noalloc(hkv.HKV_OP_STORE, P, s_ids, g.object_ptrs(s_chunks), S.cuda_stream,
+                          chunk_tokens=s_tok)
+    S.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=S):
+        g.layout.move_noalloc(hkv.HKV_OP_STORE, P, s_ids, g.object_ptrs(s_chunks),
+                              S.cuda_stream, chunk_tokens=s_tok)
+        g.layout.move_noalloc(hkv.HKV_OP_RETRIEVE, P, r_ids, g.object_ptrs(r_chunks),
+                              S.cuda_stream, chunk_tokens=r_tok)
+    used = ref.summary["pool_bytes_used"]
+    slots = list(dict.fromkeys(list(s_chunks) + list(r_chunks)))
+    for rep in range(3):
+        seed = W.derive_seed(cfg.seed, 7300 + rep)
+        pool_ref = W.fill_bytes(seed, 0, used)
+        g.pool[:used].copy_(torch.from_numpy(pool_ref))
+        objs_ref = {}
+        for i, rc in enumerate(slots):
+            objs_ref[rc] = [W.fill_bytes(W.derive_seed(seed, 1 + 4 * i + o), 0, ref.obj_bytes(o))
+                            for o in range(ref.O)]
+            for o in range(ref.O):
+                g.object_view(rc, o).copy_(torch.from_numpy(objs_ref[rc][o]))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref.store(pool_ref, s_ids, [objs_ref[rc] for rc in s_chunks], chunk_tokens=s_tok)
+        ref.retrieve(pool_ref, r_ids, [objs_ref[rc] for rc in r_chunks], chunk_tokens=r_tok)
+        assert np.array_equal(g.host_pool()[:used], pool_ref), f"pool differs on replay {rep}"
+        for rc in slots:
+            for o in range(ref.O):
+                assert np.array_equal(g.host_object(rc, o), objs_ref[rc][o]), \
+                    f"object {rc}/{o} differs on replay {rep}"
+    del graph, g
+    torch.cuda.empty_cache()

@@ -20,12 +20,18 @@ def _align(x: int, a: int = 256) -> int:
 class GpuWorkload:
     def __init__(self, cfg: W.Config, device: str = "cuda:0", tile_bytes: int = 0,
                  max_workgroups: int = 0, stream: torch.cuda.Stream | None = None,
-                 objects: str = "device", retrieve_engine: str | None = None):
+                 objects: str = "device", retrieve_engine: str | None = None,
+                 entry: str = "workspace"):
         """objects: "device" (HBM) or "host" (pinned host memory, which the
         GPU reads and writes over the host link).  retrieve_engine: "kernel"
-        or "dma" (default: the workload's own choice, else "kernel")."""
+        or "dma" (default: the workload's own choice, else "kernel").
+        entry: "workspace" (hkv_store_chunks / hkv_retrieve_chunks) or
+        "noalloc" (hkv_move_chunks_noalloc; kernel engine only)."""
         if objects not in ("device", "host"):
             raise ValueError("objects must be 'device' or 'host'")
+        if entry not in ("workspace", "noalloc"):
+            raise ValueError("entry must be 'workspace' or 'noalloc'")
+        self.entry = entry
         self.cfg = cfg
         self.objects_on = objects
         engine = retrieve_engine or cfg.extra.get("retrieve_engine", "kernel")
@@ -123,6 +129,11 @@ class GpuWorkload:
 
     def run_wave(self, w: W.Wave) -> None:
         ptrs = self.object_ptrs(w.chunks)
+        if self.entry == "noalloc":
+            op = hkv.HKV_OP_STORE if w.op == "store" else hkv.HKV_OP_RETRIEVE
+            self.layout.move_noalloc(op, self.pool.data_ptr(), w.ids, ptrs,
+                                     self.stream_of(w).cuda_stream, chunk_tokens=w.chunk_tokens)
+            return
         fn = self.layout.store if w.op == "store" else self.layout.retrieve
         second = self.duplex and w.op == "retrieve"
         ws = self.ws2 if second else self.ws
