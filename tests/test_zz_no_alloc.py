@@ -287,3 +287,40 @@ def test_noalloc_graph_capture_replays(name):
                     f"object {rc}/{o} differs on replay {rep}"
     del graph, g
     torch.cuda.empty_cache()
+
+
+def test_noalloc_capture_refuses_a_layout_not_in_the_scratch():
+    """Under capture, a no-allocation call whose layout's tables are not in
+    the static scratch (another layout's are) returns HKV_E_CAPTURE and
+    enqueues nothing: the captured graph replays only the caller's own work,
+    and the pool and objects keep their bytes."""
+    import retrieve_store_chunk_amd as hkv
+    a = Twin(W.make_config("tiny").desc, 4, 0x5EED0B)
+    b = Twin(many_blocks_desc(), 4, 0x5EED0C)
+    rng = np.random.default_rng(0x5EED0D)
+    S = a.stream
+    # the scratch now holds b's tables
+    b.call("store", _ids(rng, 4, b.lay.G, b.lay.k, b.info["num_blocks"], distinct=True),
+           list(range(4)))
+    torch.cuda.synchronize()
+    ids = _ids(rng, 4, a.lay.G, a.lay.k, a.info["num_blocks"], distinct=True)
+    pool0 = a.pools[1].clone()
+    objs0 = [x.clone() for x in a.objs[1]]
+    x = torch.zeros(16, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=S):
+        x.add_(1)
+        st_store = hkv.status_of(a.lay.move_noalloc, hkv.HKV_OP_STORE, a.pools[1].data_ptr(), ids,
+                                 a.ptrs(1, range(4)), S.cuda_stream)
+        st_retrieve = hkv.status_of(a.lay.move_noalloc, hkv.HKV_OP_RETRIEVE,
+                                    a.pools[1].data_ptr(), ids, a.ptrs(1, range(4)),
+                                    S.cuda_stream)
+    assert st_store == st_retrieve == hkv.HKV_E_CAPTURE
+    assert "another layout" in hkv.hkv_last_error()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(x.cpu(), torch.ones(16))
+    assert torch.equal(a.pools[1], pool0)
+    assert all(torch.equal(u, v) for u, v in zip(a.objs[1], objs0))
+    # outside capture the same call takes the scratch over and runs
+    a.call("store", ids, list(range(4)))
