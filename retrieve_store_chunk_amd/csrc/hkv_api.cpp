@@ -350,6 +350,23 @@ hkv::CopyArgs base_args(const hkv::Plan& p, const void* pool, const uint8_t* lay
   return a;
 }
 
+// An INT8 store whose objects are in pinned host memory writes each row's
+// codes with line-wide stores (hkv_copy.hip), which the host link carries
+// in fewer requests; in device memory the plain form is faster.  The first
+// object pointer decides (the bytes written are the same either way).  A
+// pointer the runtime cannot place leaves the plain form, and the query's
+// own error is cleared, unless the thread already had one pending.
+uint32_t codec_line_codes(const hkv::Plan& p, bool store, const hkv_chunk_batch* b) {
+  if (!store || !p.kda_codec || b->n_chunks <= 0) return 0;
+  if (hipPeekAtLastError() != hipSuccess) return 0;
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, b->objects[0]) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return attr.type == hipMemoryTypeHost ? 1u : 0u;
+}
+
 // Enqueues one launch: one workgroup per work item, unless capped by the
 // caller or by the 32-bit grid size (workgroups x threads); workgroups then
 // loop over items.
@@ -476,6 +493,7 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   const bool has_tokens = b->chunk_tokens != nullptr;
   hkv::CopyArgs a =
       base_args(p, pool, tables, tables + layer_table_bytes(p), per_chunk, n, has_tokens);
+  a.codec_line_codes = codec_line_codes(p, store, b);
   const char* entry = store ? "hkv_store_chunks" : "hkv_retrieve_chunks";
   // Per-call tables: in the kernel arguments when they fit (no copy ahead of
   // the launch), else uploaded into the workspace.
@@ -592,6 +610,7 @@ hkv_status move_noalloc(bool store, const hkv_layout* layout, void* pool,
   const uint64_t O = (uint64_t)p.n_obj_groups;
   const uint8_t* layers = scratch;
   const uint8_t* items = scratch + layer_table_bytes(p);
+  const uint32_t line_codes = codec_line_codes(p, store, b);
   uint64_t launches = 0;
   for (uint64_t c0 = 0; c0 < n; c0 += per_launch) {
     const uint64_t m = std::min(per_launch, n - c0);
@@ -602,6 +621,7 @@ hkv_status move_noalloc(bool store, const hkv_layout* layout, void* pool,
     part.chunk_tokens = has_tokens ? b->chunk_tokens + c0 : nullptr;
     part.engine = HKV_ENGINE_KERNEL;
     hkv::CopyArgs a = base_args(p, pool, layers, items, p.items.size(), m, has_tokens);
+    a.codec_line_codes = line_codes;
     hkv::InlineTables t;
     if (!hkv::pack_inline_tables(p, part, &t, &a))
       return set_error(HKV_E_ARG, "internal: a launch's tables do not fit its arguments");

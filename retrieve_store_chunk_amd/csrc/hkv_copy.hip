@@ -129,6 +129,23 @@ __device__ __forceinline__ void store4(HKV_GLOBAL uint32_t* p, uint32_t v) {
   __builtin_nontemporal_store(v, p);
 }
 
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+// kVecs consecutive 4-byte words at p (aligned to their total width).
+template <uint32_t kVecs>
+__device__ __forceinline__ void store_words(HKV_GLOBAL uint32_t* p, const uint32_t (&w)[kVecs]) {
+  static_assert(kVecs == 1 || kVecs == 2 || kVecs == 4, "code words per lane");
+  if constexpr (kVecs == 1) {
+    store4(p, w[0]);
+  } else if constexpr (kVecs == 2) {
+    const v2u v = {w[0], w[1]};
+    __builtin_nontemporal_store(v, (HKV_GLOBAL v2u*)p);
+  } else {
+    const v4u v = {w[0], w[1], w[2], w[3]};
+    store16((HKV_GLOBAL v4u*)p, v);
+  }
+}
+
 __device__ __forceinline__ float as_float(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_uint(float f) { return __builtin_bit_cast(uint32_t, f); }
 
@@ -169,13 +186,17 @@ __device__ __forceinline__ float row_max(float m) {
 // nontemporal half-line followed much later by its other half makes the
 // line leave L2 in extra pieces: 2-5% more bytes written).  Lane 0 of the
 // row writes the row's scale with an ordinary store, so that the 4-byte
-// scales of neighbouring items merge in L2 into whole lines.
+// scales of neighbouring items merge in L2 into whole lines.  When the
+// objects are in host memory (kLine: the *_line gathers) the row's lanes
+// first exchange code words, and each lane writes its run of adjacent words with
+// one store: on the host link a row's codes then travel as one request
+// instead of kVecs partial ones.
 // Retrieve: q * s back.
 // Quantisation (both sides of the parity tests take it in fp32, IEEE
 // division and round-half-even): s = max|x| / 127; q = rint(x / s) clamped
 // to [-127, 127]; 0 for non-finite x or s == 0 (Mooncake K3 blog, Compressed
 // Checkpoint Storage: per-channel INT8 of inactive recurrent states).
-template <uint32_t kD, bool kStore>
+template <uint32_t kD, bool kStore, bool kLine>
 __device__ __forceinline__ void codec_rows(const hkv::CopyArgs& a,
                                            const HKV_CONST hkv::DevLayer* L, int32_t id,
                                            uint8_t* obj_page, uint32_t group) {
@@ -228,9 +249,31 @@ __device__ __forceinline__ void codec_rows(const hkv::CopyArgs& a,
           packed[v] |= ((uint32_t)q & 0xFFu) << (8 * i);
         }
       }
+      if constexpr (kLine) {
+        // Objects in host memory: the host link carries a row's codes best
+        // as one contiguous run, so the row's lanes swap words first (LDS
+        // permutes inside the wave; a row's lanes are one aligned group).
+        const uint32_t base = (threadIdx.x & 63u) - sub;
+        const uint32_t slot = hkv::codec_word_vector(hkv::codec_line_word(sub, 0, kVecs), kLanes);
+        uint32_t line[kVecs];
 #pragma unroll
-      for (uint32_t v = 0; v < kVecs; ++v)
-        store4(qp + hkv::codec_input_vector(sub, v, kLanes), packed[v]);
+        for (uint32_t i = 0; i < kVecs; ++i) {
+          const uint32_t w = hkv::codec_line_word(sub, i, kVecs);
+          const int src = (int)((base + hkv::codec_word_lane(w, kLanes)) * 4u);
+          uint32_t x = 0;
+#pragma unroll
+          for (uint32_t v = 0; v < kVecs; ++v) {
+            const uint32_t y = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)packed[v]);
+            x = v == slot ? y : x;
+          }
+          line[i] = x;
+        }
+        store_words<kVecs>(qp + hkv::codec_line_word(sub, 0, kVecs), line);
+      } else {
+#pragma unroll
+        for (uint32_t v = 0; v < kVecs; ++v)
+          store4(qp + hkv::codec_input_vector(sub, v, kLanes), packed[v]);
+      }
       if (sub == 0) *sp = as_uint(scale);
     } else {
       uint32_t packed[kVecs];
@@ -256,7 +299,7 @@ __device__ __forceinline__ void codec_rows(const hkv::CopyArgs& a,
 // quantise or dequantise rows of kD values.  One kernel per head_dim keeps
 // each kernel's registers to what its own codec path needs (more waves in
 // flight than a kernel holding every head_dim).
-template <bool kStore, uint32_t kUnroll, uint32_t kRun, uint32_t kD>
+template <bool kStore, uint32_t kUnroll, uint32_t kRun, uint32_t kD, bool kLine = false>
 __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a, const hkv::InlineTables& t) {
   const HKV_CONST hkv::DevLayer* layers = (const HKV_CONST hkv::DevLayer*)a.layers;
   const HKV_CONST uint64_t* items = (const HKV_CONST uint64_t*)a.items;
@@ -282,7 +325,7 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a, const hkv::In
     uint8_t* obj = reinterpret_cast<uint8_t*>(objs[(uint64_t)c * a.n_obj_groups + L->obj_group]);
     uint8_t* obj_page = obj + L->obj_offset + (uint64_t)j * L->obj_page;
     if (hkv::item_kind(w)) {  // a codec row group of a KDA page (INT8 layouts only)
-      if constexpr (kD != 0) codec_rows<kD, kStore>(a, L, id, obj_page, hkv::item_index(w));
+      if constexpr (kD != 0) codec_rows<kD, kStore, kLine>(a, L, id, obj_page, hkv::item_index(w));
       continue;
     }
     // the page (or the conv part under the codec): this tile's bytes, and
@@ -308,7 +351,9 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a, const hkv::In
 }  // namespace
 
 // The gather (store) and scatter (retrieve) kernels: one pair for layouts
-// without the codec, and one pair per head_dim for INT8 layouts.
+// without the codec, and one pair per head_dim for INT8 layouts, whose
+// gather also comes in a line-code form for objects in host memory (a
+// separate kernel, so that the form for device memory keeps its registers).
 #define HKV_KERNEL_PAIR(suffix, kD)                                            \
   extern "C" __global__ __launch_bounds__(kThreads) void                       \
       hkv_store_gather##suffix(hkv::CopyArgs a, hkv::InlineTables t) {         \
@@ -318,6 +363,11 @@ __device__ __forceinline__ void copy_items(const hkv::CopyArgs& a, const hkv::In
       hkv_retrieve_scatter##suffix(hkv::CopyArgs a, hkv::InlineTables t) {     \
     copy_items<false, kRetrieveUnroll, kRetrieveXcdRun, kD>(a, t);             \
   }
+#define HKV_LINE_GATHER(suffix, kD)                                            \
+  extern "C" __global__ __launch_bounds__(kThreads) void                       \
+      hkv_store_gather##suffix##_line(hkv::CopyArgs a, hkv::InlineTables t) {  \
+    copy_items<true, kStoreUnroll, kStoreXcdRun, kD, true>(a, t);              \
+  }
 
 HKV_KERNEL_PAIR(, 0)
 HKV_KERNEL_PAIR(_int8_d16, 16)
@@ -325,7 +375,13 @@ HKV_KERNEL_PAIR(_int8_d32, 32)
 HKV_KERNEL_PAIR(_int8_d64, 64)
 HKV_KERNEL_PAIR(_int8_d128, 128)
 HKV_KERNEL_PAIR(_int8_d256, 256)
+HKV_LINE_GATHER(_int8_d16, 16)
+HKV_LINE_GATHER(_int8_d32, 32)
+HKV_LINE_GATHER(_int8_d64, 64)
+HKV_LINE_GATHER(_int8_d128, 128)
+HKV_LINE_GATHER(_int8_d256, 256)
 #undef HKV_KERNEL_PAIR
+#undef HKV_LINE_GATHER
 
 namespace hkv {
 
@@ -349,28 +405,31 @@ int static_scratch(int dev, uint8_t** ptr) {
 int launch_copy(bool store, const CopyArgs& a, const InlineTables& t, uint32_t grid,
                 void* stream) {
   if (grid == 0) return 0;
-  struct Pair {
+  struct Kernels {
     uint32_t head_dim;
     const void* store;
     const void* retrieve;
+    const void* store_line;  // INT8 layouts: line-code gather (objects in host memory)
   };
-  static const Pair kPairs[] = {
-      {0, reinterpret_cast<const void*>(&hkv_store_gather),
-       reinterpret_cast<const void*>(&hkv_retrieve_scatter)},
-      {16, reinterpret_cast<const void*>(&hkv_store_gather_int8_d16),
-       reinterpret_cast<const void*>(&hkv_retrieve_scatter_int8_d16)},
-      {32, reinterpret_cast<const void*>(&hkv_store_gather_int8_d32),
-       reinterpret_cast<const void*>(&hkv_retrieve_scatter_int8_d32)},
-      {64, reinterpret_cast<const void*>(&hkv_store_gather_int8_d64),
-       reinterpret_cast<const void*>(&hkv_retrieve_scatter_int8_d64)},
-      {128, reinterpret_cast<const void*>(&hkv_store_gather_int8_d128),
-       reinterpret_cast<const void*>(&hkv_retrieve_scatter_int8_d128)},
-      {256, reinterpret_cast<const void*>(&hkv_store_gather_int8_d256),
-       reinterpret_cast<const void*>(&hkv_retrieve_scatter_int8_d256)},
+#define HKV_FN(f) reinterpret_cast<const void*>(&f)
+  static const Kernels kKernels[] = {
+      {0, HKV_FN(hkv_store_gather), HKV_FN(hkv_retrieve_scatter), nullptr},
+      {16, HKV_FN(hkv_store_gather_int8_d16), HKV_FN(hkv_retrieve_scatter_int8_d16),
+       HKV_FN(hkv_store_gather_int8_d16_line)},
+      {32, HKV_FN(hkv_store_gather_int8_d32), HKV_FN(hkv_retrieve_scatter_int8_d32),
+       HKV_FN(hkv_store_gather_int8_d32_line)},
+      {64, HKV_FN(hkv_store_gather_int8_d64), HKV_FN(hkv_retrieve_scatter_int8_d64),
+       HKV_FN(hkv_store_gather_int8_d64_line)},
+      {128, HKV_FN(hkv_store_gather_int8_d128), HKV_FN(hkv_retrieve_scatter_int8_d128),
+       HKV_FN(hkv_store_gather_int8_d128_line)},
+      {256, HKV_FN(hkv_store_gather_int8_d256), HKV_FN(hkv_retrieve_scatter_int8_d256),
+       HKV_FN(hkv_store_gather_int8_d256_line)},
   };
+#undef HKV_FN
   const void* fn = nullptr;
-  for (const Pair& k : kPairs)
-    if (k.head_dim == a.codec_head_dim) fn = store ? k.store : k.retrieve;
+  for (const Kernels& k : kKernels)
+    if (k.head_dim == a.codec_head_dim)
+      fn = !store ? k.retrieve : (a.codec_line_codes && k.store_line) ? k.store_line : k.store;
   if (!fn) return (int)hipErrorInvalidValue;  // the planner admits no other head_dim
   CopyArgs arg = a;
   void* params[] = {&arg, const_cast<InlineTables*>(&t)};

@@ -92,6 +92,18 @@ inline constexpr uint32_t codec_input_vector(uint32_t sub, uint32_t v, uint32_t 
   return sub + v * lanes;
 }
 
+// Line-wide code stores (a store whose objects are in host memory): the
+// lanes of a row first exchange code words so that lane `sub` holds words
+// vecs * sub + i, i < vecs, of the row, then writes them with one store of
+// 4 * vecs bytes; the row's codes leave as one contiguous run from one
+// instruction.  Word w of a row sits, before the exchange, in lane
+// w % lanes as its vector w / lanes (codec_input_vector).
+inline constexpr uint32_t codec_line_word(uint32_t sub, uint32_t i, uint32_t vecs) {
+  return sub * vecs + i;
+}
+inline constexpr uint32_t codec_word_lane(uint32_t w, uint32_t lanes) { return w % lanes; }
+inline constexpr uint32_t codec_word_vector(uint32_t w, uint32_t lanes) { return w / lanes; }
+
 // The work item that workgroup b of a grid of `grid` workgroups takes first
 // (it then strides by `grid`).  Workgroup b runs on XCD b % xcds.
 //   run == 0: XCD x takes one contiguous range of the items, so the
@@ -136,6 +148,7 @@ struct CopyArgs {
   uint32_t n_obj_groups;
   uint32_t has_tokens;     // 0: every chunk is whole
   uint32_t inline_ids, inline_objs, inline_tokens;  // word offsets into InlineTables
+  uint32_t codec_line_codes;  // INT8 store: run the line-code gather (objects in host memory)
 };
 
 // A call's block ids, object addresses and token counts, when they fit, travel

@@ -5,7 +5,8 @@
 // or a codec item's 16-byte row loads, 4-byte code words and row scale) stay
 // inside their page, row and object, are aligned for their width, and every
 // object byte is written exactly once.  The DPP partners of the codec's row
-// reduction stay inside the row's lanes.
+// reduction stay inside the row's lanes, and so do the lanes that hand over
+// code words for line-wide code stores (holding the words they hand over).
 // Layouts: the five workloads' shapes and small ones with head_dim 16..256,
 // three tile sizes, with and without the INT8 codec, with and without null
 // ids and partial chunks.
@@ -22,7 +23,7 @@ static std::vector<uint8_t> k393() { std::vector<uint8_t> v; for (int i=0;i<92;i
 
 #define FAIL(...) do { printf("%s: ", name); printf(__VA_ARGS__); printf("\n"); return 1; } while (0)
 
-int check(const char* name, std::vector<uint8_t> is_mla, int heads, int d, int conv, int mlab, int path, uint64_t pool, int64_t N, int64_t cmin, int n_chunks, uint64_t tile, int codec, bool nulls) {
+int check(const char* name, std::vector<uint8_t> is_mla, int heads, int d, int conv, int mlab, int path, uint64_t pool, int64_t N, int64_t cmin, int n_chunks, uint64_t tile, int codec, bool nulls, bool line = false) {
   hkv_layout_desc desc{}; desc.model.n_layers = is_mla.size(); desc.model.is_mla = is_mla.data();
   desc.model.kda_heads=heads; desc.model.kda_head_dim=d; desc.model.kda_state_bytes=4; desc.model.conv_dim=conv; desc.model.conv_kernel=4; desc.model.conv_bytes=2; desc.model.mla_width=576; desc.model.mla_bytes=mlab;
   desc.block_size=N; desc.chunk_min_tokens=cmin; desc.path=path; desc.separate_object_groups=1; desc.pool_bytes=pool; desc.tile_bytes=tile; desc.kda_codec=codec;
@@ -91,12 +92,31 @@ int check(const char* name, std::vector<uint8_t> is_mla, int heads, int d, int c
             if (x % 16) FAIL("unaligned 16-B load");
             if (x < rec + (uint64_t)rr*dd*4 || x + 16 > rec + (uint64_t)(rr+1)*dd*4) FAIL("load leaves its row");
             if (x + 16 > L.pool_offset + (uint64_t)id*L.stride + L.page || x + 16 > p.pool_used) FAIL("load past page");
+            moved += 16;
+            if (line) continue;
             // the 4 codes of that vector: one 4-byte word of the row's codes
             const uint64_t q = codes + (uint64_t)rr*dd + (uint64_t)vi*4;
             if (q % 4) FAIL("unaligned code store");
             if (q < codes + (uint64_t)rr*dd || q + 4 > codes + (uint64_t)(rr+1)*dd) FAIL("code store leaves its row");
             if (int e = mark(cv, q, 4)) FAIL("code store %s", e==1?"overflow":"twice");
-            moved += 16;
+          }
+          if (line) {
+            // line-wide codes: lane sub collects words codec_line_word(sub, i) from the
+            // lanes that hold them (inside the row's aligned lane group, as the vector
+            // the kernel selects), then writes them with one 4*vecs-byte store
+            if (vecs != 1 && vecs != 2 && vecs != 4) FAIL("line store width %u", vecs);
+            const uint32_t slot = hkv::codec_word_vector(hkv::codec_line_word(sub, 0, vecs), lpr);
+            for (uint32_t i = 0; i < vecs; i++) {
+              const uint32_t w = hkv::codec_line_word(sub, i, vecs);
+              const uint32_t src = (t & 63u) - sub + hkv::codec_word_lane(w, lpr);
+              if (src / lpr != (t & 63u) / lpr) FAIL("word source leaves the row");
+              if (hkv::codec_word_vector(w, lpr) != slot) FAIL("a lane's words span two vectors");
+              if (hkv::codec_input_vector(src % lpr, slot, lpr) != w) FAIL("source does not hold word");
+            }
+            const uint64_t q = codes + (uint64_t)rr*dd + (uint64_t)hkv::codec_line_word(sub, 0, vecs)*4;
+            if (q % (4*vecs)) FAIL("unaligned line store");
+            if (q < codes + (uint64_t)rr*dd || q + 4*vecs > codes + (uint64_t)(rr+1)*dd) FAIL("line store leaves its row");
+            if (int e = mark(cv, q, 4*vecs)) FAIL("line store %s", e==1?"overflow":"twice");
           }
           if (sub == 0) { if (int e = mark(cv, scales + (uint64_t)rr*4, 4)) FAIL("scale store %s", e==1?"overflow":"twice"); }
         }
@@ -117,19 +137,23 @@ int check(const char* name, std::vector<uint8_t> is_mla, int heads, int d, int c
     moved += live;
   }
   for (auto& cv : cover) if (std::find(cv.begin(), cv.end(), 0) != cv.end()) FAIL("object byte not written");
-  printf("%-12s codec %d nulls %d ok: %llu items (%llu per chunk, %llu codec), %llu live bytes, tile %llu, rows/item %u\n", name, codec, (int)nulls, (unsigned long long)total, (unsigned long long)ipc, (unsigned long long)codec_items, (unsigned long long)moved, (unsigned long long)p.tile_bytes, p.codec_rows_per_item);
+  printf("%-12s codec %d%s nulls %d ok: %llu items (%llu per chunk, %llu codec), %llu live bytes, tile %llu, rows/item %u\n", name, codec, line ? " (line codes)" : "", (int)nulls, (unsigned long long)total, (unsigned long long)ipc, (unsigned long long)codec_items, (unsigned long long)moved, (unsigned long long)p.tile_bytes, p.codec_rows_per_item);
   return 0;
 }
 int main() {
   int bad = 0;
-  for (int codec : {0, 1}) for (bool nulls : {false, true})
+  // codec 2: the INT8 codec with line-wide code stores (objects in host memory)
+  for (int codec : {0, 1, 2}) for (bool nulls : {false, true})
   for (uint64_t tile : {0ull, 8192ull, 1ull<<20}) {
-    bad |= check("tiny", {0,0,0,1}, 2, 16, 96, 2, 0, 64ull*16*576*2, 0, 1, 16, tile, codec, nulls);
-    bad |= check("tiny_d256", {0,0,0,1}, 1, 256, 96, 2, 1, 1ull<<28, 0, 1, 4, tile, codec, nulls);
-    bad |= check("tiny_d32", {0,1,0,1}, 3, 32, 8, 2, 0, 1ull<<27, 0, 40, 5, tile, codec, nulls);
-    bad |= check("kl_tp2", kimi27(), 16, 128, 6144, 2, 0, 16ull<<30, 0, 1, 3, tile, codec, nulls);
-    bad |= check("kl_tp1", kimi27(), 32, 128, 12288, 2, 1, 64ull<<30, 0, 1, 3, tile, codec, nulls);
-    bad |= check("k3_tp8", k393(), 6, 128, 2304, 1, 0, 24ull<<30, 768, 1500, 2, tile, codec, nulls);
+    const int c = codec ? 1 : 0;
+    const bool line = codec == 2;
+    bad |= check("tiny", {0,0,0,1}, 2, 16, 96, 2, 0, 64ull*16*576*2, 0, 1, 16, tile, c, nulls, line);
+    bad |= check("tiny_d256", {0,0,0,1}, 1, 256, 96, 2, 1, 1ull<<28, 0, 1, 4, tile, c, nulls, line);
+    bad |= check("tiny_d32", {0,1,0,1}, 3, 32, 8, 2, 0, 1ull<<27, 0, 40, 5, tile, c, nulls, line);
+    bad |= check("tiny_d64", {0,1,0}, 3, 64, 104, 2, 0, 1ull<<27, 0, 40, 5, tile, c, nulls, line);
+    bad |= check("kl_tp2", kimi27(), 16, 128, 6144, 2, 0, 16ull<<30, 0, 1, 3, tile, c, nulls, line);
+    bad |= check("kl_tp1", kimi27(), 32, 128, 12288, 2, 1, 64ull<<30, 0, 1, 3, tile, c, nulls, line);
+    bad |= check("k3_tp8", k393(), 6, 128, 2304, 1, 0, 24ull<<30, 768, 1500, 2, tile, c, nulls, line);
   }
   return bad;
 }

@@ -335,7 +335,7 @@ CODEC_EDGE = [
     # d = 64, two blocks per chunk, conv part of several tiles
     mini_config("codec_d64_k2", [0, 1, 0], 0, heads=3, head_dim=64, conv_dim=104,
                 mla_width=1024, mla_bytes=2, chunk_min=40, blocks=30, codec=1),
-    # d = 256 (a whole wavefront per row), one object for every layer
+    # d = 256 (16 lanes a row, 4 vectors a lane), one object for every layer
     mini_config("codec_d256_merged", [0, 0, 1], 1, sep=0, heads=1, head_dim=256, conv_dim=8,
                 mla_width=512, mla_bytes=2, blocks=16, codec=1),
     mini_config("codec_only_kda", [0, 0, 0], 1, heads=2, head_dim=16, conv_dim=8, blocks=9,
@@ -417,6 +417,15 @@ def test_codec_host_objects():
     cfg = W.make_small_config("kl_tp1_int8_host")
     assert cfg.extra["objects"] == "host" and cfg.desc["kda_codec"] == 1
     run_parity(cfg, objects="host")
+
+
+@pytest.mark.parametrize("cfg", CODEC_EDGE + [holes_and_tails(CODEC_EDGE[2], 3, 33)],
+                         ids=lambda c: c.name)
+def test_codec_edge_layouts_host_objects(cfg):
+    """Stores into objects in pinned host memory write each row's codes with
+    line-wide stores after a lane exchange: every head_dim (1, 2 or 4 code
+    words a lane), null pages and partial chunks, against the oracle."""
+    run_parity(cfg, objects="host", pool_fill=codec_fill(cfg.desc))
 
 
 @pytest.mark.parametrize("cfg", [varied_tails(mini_config("varied", [0, 1, 0, 1], 1, chunk_min=40,
@@ -575,7 +584,7 @@ def test_dma_retrieve_parity(case):
 # ------------------------------------------------------------ graph capture
 GRAPH_CASES = [("tiny", "kernel"), ("kl_tp1", "kernel"), ("kl_tp1", "dma"),
                ("kl_tp1_tails", "kernel"), ("k3_tp8_holes", "kernel"),
-               ("kl_tp1_int8", "kernel")]
+               ("kl_tp1_int8", "kernel"), ("kl_tp1_int8_host", "kernel")]
 
 
 def _first_calls(g, m):
@@ -599,7 +608,7 @@ def test_graph_capture_replays_small_calls(name, engine):
     from workloads.runner import GpuWorkload
     cfg = W.make_config(name) if name == "tiny" else W.make_small_config(name)
     _log(f"[graph] {name} retrieve={engine}")
-    g = GpuWorkload(cfg, retrieve_engine=engine)
+    g = GpuWorkload(cfg, retrieve_engine=engine, objects=cfg.extra.get("objects", "device"))
     ref = oracle.Layout(cfg.desc)
     (s_chunks, s_ids, s_tok), (r_chunks, r_ids, r_tok) = _first_calls(g, 8)
     h, P, WS, wsb, S = g.layout.handle, g.pool.data_ptr(), g.ws.data_ptr(), g.ws_bytes, g.stream
