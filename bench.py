@@ -463,7 +463,9 @@ def main() -> int:
     # INT8 layouts run the kernel pair built for their KDA head_dim
     sfx = f"_int8_d{cfg.desc['kda_head_dim']}" if info.get("kda_codec") else ""
     for i, w in enumerate(g.waves if graph is None else ()):
-        name = ("hkv_store_gather" + sfx if w.op == "store" else
+        # an INT8 store into host memory runs the line-code form of the gather
+        line = "_line" if (sfx and on_host) else ""
+        name = ("hkv_store_gather" + sfx + line if w.op == "store" else
                 "retrieve_dma_copies" if g.retrieve_engine else "hkv_retrieve_scatter" + sfx)
         ms = [evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]
         k = kern.setdefault(name, {"launches": 0, "ms": 0.0, "hbm": 0, "link": 0})
