@@ -351,15 +351,13 @@ def main() -> int:
     cfg = W.make_config(args.config)
     log(f"workload {cfg.name}: {cfg.title}")
     objects_on = cfg.extra.get("objects", "device")
-    if args.entry == "noalloc" and args.retrieve_engine == "dma":
-        print("--entry noalloc runs the kernel engine only", file=sys.stderr)
+    engine = args.retrieve_engine or cfg.extra.get("retrieve_engine", "kernel")
+    if args.entry == "noalloc" and engine == "dma":
+        print(f"--entry noalloc runs the kernel engine only; {cfg.name} would retrieve by DMA "
+              f"(pass --retrieve-engine kernel)", file=sys.stderr)
         return 2
     g = GpuWorkload(cfg, tile_bytes=args.tile_bytes, max_workgroups=args.max_workgroups,
                     objects=objects_on, retrieve_engine=args.retrieve_engine, entry=args.entry)
-    if args.entry == "noalloc" and g.retrieve_engine:
-        print(f"--entry noalloc runs the kernel engine only; {cfg.name} retrieves by DMA",
-              file=sys.stderr)
-        return 2
     info = g.info
     log(f"layout: N={info['block_size']} C={info['chunk_tokens']} k={info['blocks_per_chunk']} "
         f"blocks={info['num_blocks']} stride={info['block_stride']} "

@@ -91,3 +91,13 @@ def test_ceiling_flags_parse():
     assert not a.no_ceilings
     a = ap.parse_args(["--no-ceilings", "--copy-ceiling"])
     assert a.no_ceilings and a.copy_ceiling
+
+
+def test_noalloc_entry_refuses_the_dma_engine():
+    """The no-allocation entry point runs the kernels only: a workload that
+    retrieves by DMA is refused before anything is allocated."""
+    from workloads.runner import GpuWorkload
+    with pytest.raises(ValueError, match="kernels only"):
+        GpuWorkload(W.make_config("kl_tp1_host_duplex"), entry="noalloc")
+    with pytest.raises(ValueError, match="kernels only"):
+        GpuWorkload(W.make_config("kl_tp1"), entry="noalloc", retrieve_engine="dma")

@@ -37,6 +37,8 @@ class GpuWorkload:
         engine = retrieve_engine or cfg.extra.get("retrieve_engine", "kernel")
         if engine not in ("kernel", "dma"):
             raise ValueError("retrieve_engine must be 'kernel' or 'dma'")
+        if entry == "noalloc" and engine == "dma":
+            raise ValueError("the no-allocation entry point runs the kernels only")
         self.retrieve_engine = hkv.HKV_ENGINE_DMA if engine == "dma" else hkv.HKV_ENGINE_KERNEL
         self.device = torch.device(device)
         desc = dict(cfg.desc, tile_bytes=tile_bytes, max_workgroups=max_workgroups)
