@@ -4,7 +4,8 @@
 // block ids of a second, zeroed pool.  Every page must come back byte for
 // byte, and nothing else in the second pool may change (the store/retrieve
 // round trip of the LMCache "Hybrid Attention Models" page: a retrieved
-// state is the stored one).
+// state is the stored one).  The same round trip then runs through the
+// no-allocation entry point, captured into a HIP graph and replayed.
 //
 // Build:  hipcc --offload-arch=gfx950 -O2 -std=c++17 -I include \
 //           examples/roundtrip.cpp -L retrieve_store_chunk_amd -lhkv \
@@ -13,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -139,8 +141,65 @@ int main() {
     std::fprintf(stderr, "roundtrip FAILED: first difference at pool byte %zu\n", first);
     return 1;
   }
-  std::printf("roundtrip ok: %d chunks, %zu pages, N=%lld, C=%lld, %d KV groups, %d objects\n",
-              n, pages, (long long)info.block_size, (long long)info.chunk_tokens, G, O);
+
+  // The same round trip through hkv_move_chunks_noalloc (no workspace, no
+  // allocation), captured once into a HIP graph and replayed: one eager call
+  // first puts the layout's tables into the library's static scratch, which
+  // a captured call cannot do.
+  hkv_chunk_batch bs = b, br = b;
+  bs.block_ids = store_ids.data();
+  br.block_ids = retr_ids.data();
+  HKV_OK_(hkv_move_chunks_noalloc(lay, HKV_OP_STORE, pool_a, &bs, stream));
+  HIP_OK(hipStreamSynchronize(stream));
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  HIP_OK(hipStreamBeginCapture(stream, hipStreamCaptureModeGlobal));
+  const hkv_status st_s = hkv_move_chunks_noalloc(lay, HKV_OP_STORE, pool_a, &bs, stream);
+  const hkv_status st_r = hkv_move_chunks_noalloc(lay, HKV_OP_RETRIEVE, pool_b, &br, stream);
+  HIP_OK(hipStreamEndCapture(stream, &graph));
+  HKV_OK_(st_s);
+  HKV_OK_(st_r);
+  HIP_OK(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
+  const int replays = 3;
+  for (int rep = 0; rep < replays; ++rep) {
+    // fresh destinations before each replay (cleared outside the graph)
+    HIP_OK(hipMemset(pool_b, 0, used));
+    HIP_OK(hipMemset(objs, 0, chunk_bytes * n));
+    HIP_OK(hipGraphLaunch(exec, stream));
+    HIP_OK(hipStreamSynchronize(stream));
+    HIP_OK(hipMemcpy(got.data(), pool_b, used, hipMemcpyDeviceToHost));
+    if (std::memcmp(got.data(), want.data(), used) != 0) {
+      std::fprintf(stderr, "roundtrip FAILED: graph replay %d differs\n", rep);
+      return 1;
+    }
+  }
+  // Host time to enqueue one call (validation, tables in the kernel
+  // arguments, launch), and the time of one replay of the captured pair.
+  const int reps = 200;
+  hipEvent_t e0, e1;
+  HIP_OK(hipEventCreate(&e0));
+  HIP_OK(hipEventCreate(&e1));
+  auto t0 = std::chrono::steady_clock::now();
+  for (int i = 0; i < reps; ++i) HKV_OK_(hkv_store_chunks(lay, pool_a, &bs, ws, ws_bytes, stream));
+  const double enqueue_us =
+      std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count() /
+      reps;
+  HIP_OK(hipStreamSynchronize(stream));
+  HIP_OK(hipEventRecord(e0, stream));
+  for (int i = 0; i < reps; ++i) HIP_OK(hipGraphLaunch(exec, stream));
+  HIP_OK(hipEventRecord(e1, stream));
+  HIP_OK(hipEventSynchronize(e1));
+  float ms = 0.0f;
+  HIP_OK(hipEventElapsedTime(&ms, e0, e1));
+  std::printf("roundtrip ok: %d chunks, %zu pages, N=%lld, C=%lld, %d KV groups, %d objects; "
+              "no-allocation pair as a graph: %d replays match; %.1f us to enqueue a store, "
+              "%.1f us per replay of store + retrieve\n",
+              n, pages, (long long)info.block_size, (long long)info.chunk_tokens, G, O, replays,
+              enqueue_us, 1e3 * ms / reps);
+  HIP_OK(hipEventDestroy(e0));
+  HIP_OK(hipEventDestroy(e1));
+  HIP_OK(hipGraphExecDestroy(exec));
+  HIP_OK(hipGraphDestroy(graph));
   HIP_OK(hipStreamDestroy(stream));
   HIP_OK(hipFree(pool_a));
   HIP_OK(hipFree(pool_b));

@@ -1,7 +1,8 @@
 """The C-ABI example (examples/roundtrip.cpp): a store and a retrieve through
 include/hkv.h and the HIP runtime alone, run as a process of its own.  Every
 stored page must come back byte for byte at its fresh block id and nothing
-else in the second pool may change."""
+else in the second pool may change, through the workspace entry points and
+through the no-allocation one captured into a HIP graph and replayed."""
 import os
 import subprocess
 
@@ -24,3 +25,5 @@ def test_c_abi_roundtrip_example():
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.startswith("roundtrip ok"), r.stdout
+    assert "3 replays match" in r.stdout, r.stdout
+    print(r.stdout, flush=True)
