@@ -225,7 +225,7 @@ def test_noalloc_oracle_round_trip_tiny():
 # launch configuration the benchmark times: every pool byte after every wave
 # and every object byte against the bytes rebuilt from the oracle's
 # placements (the checker of the full-size parity tests).
-NOALLOC_FULL_SIZE = ["kl_tp1", "k3_tp8_holes", "long_ctx", "kl_tp1_int8"]
+NOALLOC_FULL_SIZE = ["kl_tp1", "k3_tp8_holes", "long_ctx", "kl_tp1_int8", "kl_tp1_int8_host"]
 
 
 @pytest.mark.parametrize("name", NOALLOC_FULL_SIZE)
@@ -234,17 +234,18 @@ def test_noalloc_full_size_every_byte(name):
     run_every_byte(name, entry="noalloc")
 
 
-@pytest.mark.parametrize("name", ["tiny", "kl_tp1", "k3_tp8_holes"])
+@pytest.mark.parametrize("name", ["tiny", "kl_tp1", "k3_tp8_holes", "kl_tp1_int8_host"])
 def test_noalloc_graph_capture_replays(name):
     """A no-allocation store and retrieve captured into one HIP graph, after
     one eager call has put the layout's tables in the static scratch.  Three
     replays, with new pool and object bytes written eagerly before each, all
-    match the oracle applied to that replay's inputs."""
+    match the oracle applied to that replay's inputs.  With INT8 objects in
+    host memory the captured store is the line-code gather."""
     import retrieve_store_chunk_amd as hkv
     from workloads.runner import GpuWorkload
     cfg = W.make_config(name) if name == "tiny" else W.make_small_config(name)
     _log(f"[noalloc graph] {name}")
-    g = GpuWorkload(cfg, entry="noalloc")
+    g = GpuWorkload(cfg, entry="noalloc", objects=cfg.extra.get("objects", "device"))
     ref = oracle.Layout(cfg.desc)
     calls = []
     for op in ("store", "retrieve"):
