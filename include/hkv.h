@@ -271,7 +271,10 @@ hkv_status hkv_workspace_size(const hkv_layout* layout, int32_t max_chunks, size
  * state is one opaque page per block).
  * (obj_page_bytes = page_bytes, except KDA pages under kda_codec = 1, which
  * are written in their INT8 form).  Padding and group slack are never read.
- * The pool is not modified.
+ * The pool is not modified.  Under kda_codec = 1 the first object pointer's
+ * memory type (hipPointerGetAttributes) picks the gather: pinned host memory
+ * takes a form that writes each row's codes as one run, which the host link
+ * carries better; the bytes written are the same either way.
  * pool: DEVICE, 16-byte aligned, pool_bytes_used long.  workspace: DEVICE,
  * 16-byte aligned, ws_bytes >= hkv_workspace_size(n_chunks); it is
  * overwritten and must not be used by another call until the stream passes
