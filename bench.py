@@ -186,7 +186,8 @@ def cpu_baseline(cfg, threads: int = 1, min_seconds: float = 10.0,
             passes += 1
     gbs = passes * payload / t_wall / 1e9
     how = "single-threaded" if threads == 1 else f"{threads} host threads, chunks split evenly"
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads,
+    return {"value": round(gbs, 3), "unit": "GB/s",
+            "chunks_per_s": round(passes * (n_store + n_ret) / t_wall, 1), "cores": threads,
             "cores_available": cpu_available(), "kind": "oracle",
             "sample": f"{passes} passes of: store {n_store} chunks + retrieve {n_ret} chunks "
                       f"(same page shapes, pool of {s['num_blocks']} blocks, pool and object "

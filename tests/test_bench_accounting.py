@@ -101,3 +101,13 @@ def test_noalloc_entry_refuses_the_dma_engine():
         GpuWorkload(W.make_config("kl_tp1_host_duplex"), entry="noalloc")
     with pytest.raises(ValueError, match="kernels only"):
         GpuWorkload(W.make_config("kl_tp1"), entry="noalloc", retrieve_engine="dma")
+
+
+def test_cpu_baseline_fields_on_a_tiny_sample():
+    """The oracle leg reports GB/s and chunks/s on the seeded sample, the
+    threads it used and the CPUs available."""
+    out = bench.cpu_baseline(W.make_config("tiny"), threads=2, min_seconds=0.05, max_seconds=0.5)
+    assert out["kind"] == "oracle" and out["unit"] == "GB/s"
+    assert out["value"] > 0 and out["chunks_per_s"] > 0
+    assert out["cores"] == 2 and out["cores_available"] >= 1
+    assert "seeded generator" in out["sample"]
