@@ -325,3 +325,69 @@ def test_noalloc_capture_refuses_a_layout_not_in_the_scratch():
     assert all(torch.equal(u, v) for u, v in zip(a.objs[1], objs0))
     # outside capture the same call takes the scratch over and runs
     a.call("store", ids, list(range(4)))
+
+
+def test_noalloc_threads_share_one_layout():
+    """Four host threads, each with its own stream, pool and objects, call
+    the no-allocation entry point with one shared layout at the same time
+    (the first calls race to put its tables into the scratch; the others
+    wait for that upload).  Each thread's store and retrieve match the
+    oracle."""
+    import threading
+
+    import retrieve_store_chunk_amd as hkv
+    cfg = W.make_config("tiny")
+    lay = hkv.Layout(cfg.desc)
+    ref = oracle.Layout(cfg.desc)
+    used = ref.summary["pool_bytes_used"]
+    nb = ref.summary["num_blocks"]
+    n = 6
+    # another layout's tables in the scratch first, so the threads' first calls upload
+    other = Twin(many_blocks_desc(), 2, 0x5EED0E)
+    other.call("store", _ids(np.random.default_rng(1), 2, other.lay.G, other.lay.k,
+                             other.info["num_blocks"], distinct=True), [0, 1])
+    jobs = []
+    for t in range(4):
+        rng = np.random.default_rng(0x5EED10 + t)
+        pool_ref = W.fill_bytes(W.derive_seed(0x5EED10, t), 0, used)
+        ids = _ids(rng, n, ref.G, ref.k, nb, distinct=True)
+        ids2 = _ids(rng, n, ref.G, ref.k, nb, distinct=True)
+        jobs.append(dict(pool=torch.from_numpy(pool_ref.copy()).to("cuda"), pool_ref=pool_ref,
+                         ids=ids, ids2=ids2, stream=torch.cuda.Stream(),
+                         objs=[[torch.zeros(ref.obj_bytes(o), dtype=torch.uint8, device="cuda")
+                                for o in range(ref.O)] for _ in range(n)]))
+    torch.cuda.synchronize()
+    errors = []
+    start = threading.Barrier(4)
+
+    def run(j):
+        try:
+            ptrs = [j["objs"][c][o].data_ptr() for c in range(n) for o in range(ref.O)]
+            start.wait()
+            for _ in range(3):
+                lay.move_noalloc(hkv.HKV_OP_STORE, j["pool"].data_ptr(), j["ids"], ptrs,
+                                 j["stream"].cuda_stream)
+                lay.move_noalloc(hkv.HKV_OP_RETRIEVE, j["pool"].data_ptr(), j["ids2"], ptrs,
+                                 j["stream"].cuda_stream)
+            j["stream"].synchronize()
+        except Exception as e:  # reported after the join
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(j,)) for j in jobs]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for t, j in enumerate(jobs):
+        objs_ref = [[np.zeros(ref.obj_bytes(o), np.uint8) for o in range(ref.O)]
+                    for _ in range(n)]
+        for _ in range(3):
+            ref.store(j["pool_ref"], j["ids"], objs_ref)
+            ref.retrieve(j["pool_ref"], j["ids2"], objs_ref)
+        assert np.array_equal(j["pool"].cpu().numpy(), j["pool_ref"]), f"thread {t}: pool"
+        for c in range(n):
+            for o in range(ref.O):
+                assert np.array_equal(j["objs"][c][o].cpu().numpy(), objs_ref[c][o]), \
+                    f"thread {t}: object {c}/{o}"
