@@ -467,7 +467,11 @@ def main() -> int:
         name = ("hkv_store_gather" + sfx + line if w.op == "store" else
                 "retrieve_dma_copies" if g.retrieve_engine else "hkv_retrieve_scatter" + sfx)
         ms = [evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]
-        k = kern.setdefault(name, {"launches": 0, "ms": 0.0, "hbm": 0, "link": 0})
+        k = kern.setdefault(name, {"launches": 0, "ms": 0.0, "hbm": 0, "link": 0,
+                                   "read": 0, "write": 0})
+        data, objb, live = wave_bytes(g.layout, w)
+        k["read"] += data if w.op == "store" else live
+        k["write"] += objb if w.op == "store" else data
         k["launches"] += args.steps
         k["ms"] += sum(ms)
         k["hbm"] += per_wave_hbm[i] * args.steps
@@ -575,6 +579,20 @@ def main() -> int:
     if args.hbm_ceiling or not args.no_ceilings:
         out["hbm_ceiling"] = hbm_ceiling(g.pool, stream)
         log(f"HBM reference rates: {out['hbm_ceiling']}")
+        dk = kern.get(roofline["kernel"])
+        if roofline["bound"] == "hbm" and dk and dk.get("read", 0) + dk.get("write", 0):
+            # what this process's memory placement allows the dominant kernel:
+            # its read/write mix at the library-shaped reference rates
+            hc = out["hbm_ceiling"]
+            rs = dk["read"] / (dk["read"] + dk["write"])
+            mix = 1.0 / (rs / hc["read_GBs"] + (1.0 - rs) / hc["write_GBs"])
+            roofline["process_ceiling"] = {
+                "GBs": round(mix, 1), "frac": round(roofline["achieved"] / mix, 4),
+                "read_share": round(rs, 4),
+                "what": "the kernel's read/write mix at the read and write rates of the "
+                        "library-shaped reference kernels timed in this process"}
+            log(f"dominant kernel at {100 * roofline['achieved'] / mix:.1f}% of this "
+                f"process's read/write mix ceiling ({mix:.0f} GB/s)")
 
     del g
     torch.cuda.empty_cache()
