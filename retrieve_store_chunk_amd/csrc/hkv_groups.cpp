@@ -36,19 +36,18 @@ bool plan_grouped_retrieve(const Plan& p, const hkv_chunk_batch& b, GroupedCall*
   uint64_t n_items_total = 0;
   for (size_t g = 0; g < out->members.size(); ++g) {
     const std::vector<int32_t>& sig = signature[g];
+    const bool has_tokens = sig[G * k] >= 0;
     for (const uint64_t w : p.items) {
-      const uint32_t l = (uint32_t)(w & 0xFFFFu), j = (uint32_t)((w >> 16) & 0xFFFFu);
-      const uint64_t s = (w >> 32) & 0x7FFFFFFFull;
-      const DevLayer& L = p.dev_layers[l];
+      const uint32_t j = item_block(w);
+      const DevLayer& L = p.dev_layers[item_layer(w)];
       if (sig[L.kv_group * k + j]) continue;  // a null page
-      if ((w >> 63) == 0) {
-        uint64_t valid = L.copy_bytes;
-        if (sig[G * k] >= 0 && L.row_bytes) {
-          int64_t rows = (int64_t)sig[G * k] - (int64_t)j * p.block_size;
-          rows = rows < 0 ? 0 : (rows > p.block_size ? p.block_size : rows);
-          valid = (uint64_t)rows * L.row_bytes;
-        }
-        if (valid <= s * p.tile_bytes) continue;  // past the valid rows
+      if (item_kind(w) == 0) {
+        // the kernel's own tile arithmetic (any non-null id writes the same bytes)
+        const TileSpan ts = tile_span(
+            L.copy_bytes, item_index(w), p.tile_bytes,
+            live_span_bytes(0, L.copy_bytes, L.row_bytes, has_tokens, sig[G * k], j,
+                            (uint64_t)p.block_size));
+        if (ts.live == 0) continue;  // past the valid rows
       }
       out->items[g].push_back(w);
     }
