@@ -135,12 +135,11 @@ void plan_dma_runs(const Plan& p, const hkv_chunk_batch& b, uint64_t pool,
         for (uint64_t j = 0; j < k; ++j) {
           const int32_t id = b.block_ids[(c * G + (uint64_t)x.kv_group) * k + j];
           if (id == HKV_NULL_BLOCK) continue;
-          uint64_t live = x.page;
-          if (b.chunk_tokens && x.is_mla) {
-            int64_t rows = t - (int64_t)(j * N);
-            rows = rows < 0 ? 0 : (rows > (int64_t)N ? (int64_t)N : rows);
-            live = (uint64_t)rows * (x.page / N);
-          }
+          // (the DMA engine serves layouts without the codec: a page is copied
+          // whole, or an MLA page's valid token rows)
+          const uint64_t live =
+              live_span_bytes(id, x.page, x.is_mla ? (uint32_t)(x.page / N) : 0u,
+                              b.chunk_tokens != nullptr, t, (uint32_t)j, N);
           if (live == 0) continue;
           const uint64_t src = obj + x.obj_offset + j * x.obj_page;
           const uint64_t dst = pool + x.pool_offset + (uint64_t)id * x.stride;

@@ -42,7 +42,8 @@ static int ops_of(const char* name, const hkv::Plan& p, const uint8_t* tab, uint
   const int32_t* toks = (const int32_t*)(tab + tokens_off);
   for (uint64_t item = 0; item < n_chunks * n_items; ++item) {
     const uint64_t c = item / n_items, r = item % n_items, w = items[r];
-    const uint32_t l = w & 0xFFFF, j = (w >> 16) & 0xFFFF, s = (w >> 32) & 0x7FFFFFFF, kind = w >> 63;
+    const uint32_t l = hkv::item_layer(w), j = hkv::item_block(w), s = hkv::item_index(w);
+    const uint32_t kind = hkv::item_kind(w);
     if (l >= p.dev_layers.size() || j >= k) FAIL("bad item");
     const hkv::DevLayer& L = p.dev_layers[l];
     const int32_t id = ids[(c * G + L.kv_group) * k + j];
@@ -61,15 +62,12 @@ static int ops_of(const char* name, const hkv::Plan& p, const uint8_t* tab, uint
       out->push_back(Op(lo, (uint64_t)(r_end - r0) * L.head_dim * 4, ch, L.obj_group, obj_page + L.copy_bytes + (uint64_t)r0 * L.head_dim, 1));
       continue;
     }
-    const uint64_t off = (uint64_t)s * p.tile_bytes;
-    const uint64_t bytes = std::min<uint64_t>(L.copy_bytes - off, p.tile_bytes);
-    uint64_t valid = id < 0 ? 0 : L.copy_bytes;
-    if (has_tokens && L.row_bytes && id >= 0) {
-      int64_t rows = (int64_t)toks[c] - (int64_t)j * p.block_size;
-      rows = rows < 0 ? 0 : (rows > p.block_size ? p.block_size : rows);
-      valid = rows * L.row_bytes;
-    }
-    const uint64_t live = valid > off ? std::min<uint64_t>(valid - off, bytes) : 0;
+    // the kernels' own tile arithmetic (hkv_device_tables.hpp)
+    const hkv::TileSpan ts = hkv::tile_span(
+        L.copy_bytes, s, p.tile_bytes,
+        hkv::live_span_bytes(id, L.copy_bytes, L.row_bytes, has_tokens,
+                             has_tokens ? (int64_t)toks[c] : 0, j, (uint64_t)p.block_size));
+    const uint64_t off = ts.off, live = ts.live;
     if (!live) continue;
     const uint64_t lo = L.pool_offset + (uint64_t)id * L.stride + off;
     if (lo + live > L.pool_offset + (uint64_t)id * L.stride + L.page || lo + live > p.pool_used) FAIL("pool write past the page");
