@@ -329,15 +329,16 @@ hkv_status hkv_retrieve_chunks(const hkv_layout* layout, void* pool,
  * (op = HKV_OP_STORE) or hkv_retrieve_chunks (op = HKV_OP_RETRIEVE) with the
  * same kernels and the same bytes in the pool and objects, but no workspace
  * and no allocation.  It calls no hipMalloc, hipFree, hipHostMalloc or other
- * allocating routine, and uses no pinned staging.
+ * allocating routine, and uses none of the library's pinned staging.
  *   - The layout's constant tables live in a static device array of the
  *     library, 4 MiB per device (held from the first such call on a device
  *     until the process ends); a layout whose tables are larger (more than
  *     about 500,000 work items per chunk) gets HKV_E_WORKSPACE.
  *   - The array holds one layout's tables at a time.  A call whose layout's
- *     tables are not there copies them in from the layout's host memory and
- *     waits for `stream` to finish; later calls with the same layout on that
- *     device enqueue without waiting.  While `stream` is capturing, such a
+ *     tables are not there copies them in from the layout's host memory
+ *     (hipMemcpyAsync from pageable memory, which the HIP runtime moves
+ *     through its own staging) and waits for `stream` to finish; later calls
+ *     with the same layout on that device enqueue without waiting.  While `stream` is capturing, such a
  *     copy is refused (HKV_E_CAPTURE, nothing enqueued); a captured call
  *     reads the array when the graph replays, so no call with another layout
  *     may run on that device between capture and replay.
