@@ -419,6 +419,52 @@ def test_codec_host_objects():
     run_parity(cfg, objects="host")
 
 
+@pytest.mark.parametrize("first_on_host", [True, False], ids=["host_first", "device_first"])
+@pytest.mark.parametrize("cfg", [CODEC_EDGE[0], CODEC_EDGE[2], CODEC_EDGE[3]], ids=lambda c: c.name)
+def test_codec_store_with_objects_in_both_memories(cfg, first_on_host):
+    """An INT8 store whose objects are split between pinned host memory and
+    device memory (every other chunk): the first object picks the gather
+    form, and either form writes the oracle's bytes into both kinds of
+    memory."""
+    import retrieve_store_chunk_amd as hkv
+    ref = oracle.Layout(cfg.desc)
+    lay = hkv.Layout(cfg.desc)
+    used = ref.summary["pool_bytes_used"]
+    pool_ref = codec_fill(cfg.desc)(used, W.derive_seed(cfg.seed, 91))
+    pool = torch.from_numpy(pool_ref).to("cuda")
+    n = 6
+    rng = np.random.default_rng(0x5EED20)
+    # (a store may read one block for several chunks)
+    ids = rng.integers(0, ref.summary["num_blocks"], size=(n, ref.G, ref.k)).astype(np.int32)
+    objs = []
+    for c in range(n):
+        on_host = (c % 2 == 0) == first_on_host
+        objs.append([torch.full((ref.obj_bytes(o),), 0xA5, dtype=torch.uint8,
+                                pin_memory=True) if on_host else
+                     torch.full((ref.obj_bytes(o),), 0xA5, dtype=torch.uint8, device="cuda")
+                     for o in range(ref.O)])
+    objs_ref = [[np.full(ref.obj_bytes(o), 0xA5, np.uint8) for o in range(ref.O)]
+                for _ in range(n)]
+    ptrs = [objs[c][o].data_ptr() for c in range(n) for o in range(ref.O)]
+    ws_bytes = lay.workspace_size(n)
+    ws = torch.empty(max(256, ws_bytes), dtype=torch.uint8, device="cuda")
+    ref.store(pool_ref, ids, objs_ref)
+    for entry in ("workspace", "noalloc"):
+        for row in objs:
+            for t in row:
+                t.fill_(0xA5)
+        torch.cuda.synchronize()
+        if entry == "workspace":
+            lay.store(pool.data_ptr(), ids, ptrs, ws.data_ptr(), ws_bytes, 0)
+        else:
+            lay.move_noalloc(hkv.HKV_OP_STORE, pool.data_ptr(), ids, ptrs, 0)
+        torch.cuda.synchronize()
+        for c in range(n):
+            for o in range(ref.O):
+                assert np.array_equal(objs[c][o].cpu().numpy(), objs_ref[c][o]), \
+                    f"{entry}: object {c}/{o}"
+
+
 @pytest.mark.parametrize("cfg", CODEC_EDGE + [holes_and_tails(CODEC_EDGE[2], 3, 33)],
                          ids=lambda c: c.name)
 def test_codec_edge_layouts_host_objects(cfg):
