@@ -148,6 +148,8 @@ EDGE = [
                 mla_bytes=2, blocks=10),
     # the whole pool addressed: every id up to num_blocks - 1 is used
     mini_config("full_pool", [0, 0, 0, 1], 0, blocks=8, requests=(1, 1)),
+    # twenty blocks per chunk (a 320-token minimum at N = 16)
+    mini_config("k20_blocks", [0, 1], 1, chunk_min=320, blocks=256),
 ]
 
 
@@ -187,7 +189,8 @@ def varied_tails(cfg, tails, every=1):
 @pytest.mark.parametrize("cfg", [holes_and_tails(EDGE[0], 2, 5), holes_and_tails(EDGE[1], 1, 1),
                                  holes_and_tails(EDGE[2], 3, 33),
                                  holes_and_tails(EDGE[9], 2, 17),
-                                 holes_and_tails(EDGE[2], 1, 0)],
+                                 holes_and_tails(EDGE[2], 1, 0),
+                                 holes_and_tails(EDGE[11], 4, 150)],
                          ids=lambda c: c.name)
 def test_edge_layouts_with_holes_and_tails(cfg):
     """Null ids and partial chunks on odd page sizes (byte path), several
