@@ -387,15 +387,15 @@ hkv_status launch_one(bool store, const hkv::Plan& p, const hkv::CopyArgs& a,
 const hkv::InlineTables kNoInlineTables{};
 
 void trace_call(const char* entry, bool store, const hkv::Plan& p, const hkv_chunk_batch* b,
-                uint64_t launches, uint64_t items, const char* tables) {
+                uint64_t launches, uint64_t items, const char* tables, bool line_codes = false) {
   if (!trace_on()) return;
   std::fprintf(stderr,
                "[hkv] %s %s: %d chunks, %llu launches, %llu work items (tile %llu B), "
-               "%llu payload bytes, tables %s\n",
+               "%llu payload bytes, tables %s%s\n",
                entry, store ? "store" : "retrieve", b->n_chunks, (unsigned long long)launches,
                (unsigned long long)items, (unsigned long long)p.tile_bytes,
                (unsigned long long)((uint64_t)b->n_chunks * (p.obj_bytes[0] + p.obj_bytes[1])),
-               tables);
+               tables, line_codes ? "; line-code gather (objects in host memory)" : "");
 }
 
 // The grouped retrieve (hkv_groups.hpp): one upload of every class's tables,
@@ -501,7 +501,8 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
     hkv::InlineTables t;
     if (hkv::pack_inline_tables(p, *b, &t, &a)) {
       st = launch_one(store, p, a, t, stream);
-      if (st == HKV_OK) trace_call(entry, store, p, b, 1, a.total_items, "in the arguments");
+      if (st == HKV_OK)
+        trace_call(entry, store, p, b, 1, a.total_items, "in the arguments", a.codec_line_codes);
       return st;
     }
   }
@@ -521,7 +522,7 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
   a.objs = reinterpret_cast<const uint64_t*>(wsb + wl.objs_off);
   a.chunk_tokens = reinterpret_cast<const int32_t*>(wsb + wl.tokens_off);
   st = launch_one(store, p, a, kNoInlineTables, stream);
-  if (st == HKV_OK) trace_call(entry, store, p, b, 1, a.total_items, "staged");
+  if (st == HKV_OK) trace_call(entry, store, p, b, 1, a.total_items, "staged", a.codec_line_codes);
   return st;
 }
 
@@ -630,7 +631,7 @@ hkv_status move_noalloc(bool store, const hkv_layout* layout, void* pool,
     ++launches;
   }
   trace_call("hkv_move_chunks_noalloc", store, p, b, launches, n * p.items.size(),
-             "in the arguments; layout tables in the static scratch");
+             "in the arguments; layout tables in the static scratch", line_codes != 0);
   return HKV_OK;
 }
 

@@ -5,6 +5,8 @@ pool after every wave and every object at the end.  Inputs are generated on
 the host (workloads.fill_bytes) and copied to the device, so neither side's
 inputs come from the other.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -808,3 +810,29 @@ def test_calls_from_several_threads_at_once():
             want = np.stack([objs_ref[t][c][o] for c in range(n)])
             assert np.array_equal(got, want), f"thread {t} objects {o}"
     assert np.array_equal(pool[:used].cpu().numpy(), pool_ref), "pool"
+
+
+def test_trace_names_the_line_code_gather_for_host_objects(tmp_path):
+    """With HKV_TRACE=1, an INT8 store into pinned host memory reports the
+    line-code gather, and one into device memory does not (a child process,
+    so the trace setting is read fresh)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys, torch; sys.path.insert(0, %r)\n"
+        "import workloads as W\n"
+        "from workloads.runner import GpuWorkload\n"
+        "for objects in ('host', 'device'):\n"
+        "    g = GpuWorkload(W.make_small_config('kl_tp1_int8_host'), objects=objects)\n"
+        "    g.init_pool()\n"
+        "    w = next(w for w in g.waves if w.op == 'store')\n"
+        "    print('[objects] ' + objects, file=sys.stderr, flush=True)\n"
+        "    g.run_wave(w)\n"
+        "    torch.cuda.synchronize()\n" % root)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       env=dict(os.environ, HKV_TRACE="1"), cwd=root)
+    assert r.returncode == 0, r.stderr[-3000:]
+    host_part, device_part = r.stderr.split("[objects] host", 1)[1].split("[objects] device", 1)
+    assert "line-code gather" in host_part, host_part[-2000:]
+    assert "store" in device_part and "line-code gather" not in device_part, device_part[-2000:]
