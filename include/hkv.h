@@ -334,20 +334,29 @@ hkv_status hkv_retrieve_chunks(const hkv_layout* layout, void* pool,
  *     library, 4 MiB per device (held from the first such call on a device
  *     until the process ends); a layout whose tables are larger (more than
  *     about 500,000 work items per chunk) gets HKV_E_WORKSPACE.
- *   - The array holds one layout's tables at a time.  A call whose layout's
- *     tables are not there copies them in from the layout's host memory
- *     (hipMemcpyAsync from pageable memory, which the HIP runtime moves
- *     through its own staging) and waits for `stream` to finish; later calls
- *     with the same layout on that device enqueue without waiting.  While `stream` is capturing, such a
- *     copy is refused (HKV_E_CAPTURE, nothing enqueued); a captured call
- *     reads the array when the graph replays, so no call with another layout
- *     may run on that device between capture and replay.
+ *   - The array holds several layouts' tables at once, each in a range of
+ *     its own (about 117 KB at the Kimi-Linear shapes, so some 35 such
+ *     layouts).  A call whose layout's tables are not there copies them in
+ *     from the layout's host memory (hipMemcpyAsync from pageable memory,
+ *     which the HIP runtime moves through its own staging) and waits for
+ *     `stream` to finish; later calls with that layout on that device
+ *     enqueue without waiting.  When the array is full, the layout used
+ *     least recently is dropped to make room, except layouts that a captured
+ *     call has used.  hkv_layout_destroy frees the layout's ranges.
+ *   - While `stream` is capturing, a copy-in is refused (HKV_E_CAPTURE,
+ *     nothing enqueued): make one call with each layout on the device before
+ *     capturing.  A captured call reads its layout's tables when the graph
+ *     replays, so that layout stays in the array until it is destroyed (do
+ *     not replay the graph after that); when such layouts fill the array, a
+ *     call that needs room gets HKV_E_WORKSPACE.
  *   - The call's block ids, object addresses and token counts travel in
  *     kernel arguments: one launch per run of chunks that fits (up to 96
  *     chunks at the Kimi-Linear shapes), so a large call is several launches.
- *   - Every call on a device shares that device's array: calls that overlap
- *     on one device (other streams, other threads) with different layouts
- *     race, and must be ordered by the caller.
+ *   - Every call on a device shares that device's array.  Calls that
+ *     overlap on one device (other streams, other threads) race only when
+ *     one of them copies a layout in over the range of a layout that the
+ *     other is using (an eviction, with more layouts than fit): order such
+ *     calls.
  *   - A retrieve with null ids or partial chunks runs one launch over every
  *     work item per run of chunks (no per-class launches); the bytes written
  *     are the same.
@@ -358,8 +367,9 @@ hkv_status hkv_retrieve_chunks(const hkv_layout* layout, void* pool,
  * Errors: HKV_E_ARG (also a bad op, the DMA engine, or a chunk whose ids and
  * object addresses alone exceed the kernel-argument block), HKV_E_RANGE,
  * HKV_E_ALIAS (objects overlap each other or the pool; repeated retrieve
- * ids), HKV_E_ALIGN, HKV_E_WORKSPACE (tables larger than the static array),
- * HKV_E_CAPTURE, HKV_E_HIP. */
+ * ids), HKV_E_ALIGN, HKV_E_WORKSPACE (tables larger than the static array, or
+ * no room beside the layouts that captured calls use), HKV_E_CAPTURE,
+ * HKV_E_HIP. */
 hkv_status hkv_move_chunks_noalloc(const hkv_layout* layout, int32_t op, void* pool,
                                    const hkv_chunk_batch* batch, void* stream);
 

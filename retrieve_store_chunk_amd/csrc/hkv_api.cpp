@@ -9,8 +9,9 @@
 // copy has completed.
 //
 // hkv_move_chunks_noalloc runs the same kernels without any allocation: the
-// layout's tables go into a static device array (hkv_copy.hip) and the
-// call's tables into kernel arguments, several launches if need be.
+// layout's tables go into a static device array (hkv_copy.hip), which holds
+// several layouts' tables at once, and the call's tables into kernel
+// arguments, several launches if need be.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -29,6 +30,7 @@
 #include "hkv_groups.hpp"
 #include "hkv_launch.hpp"
 #include "hkv_plan.hpp"
+#include "hkv_scratch.hpp"
 
 struct hkv_layout {
   hkv::Plan plan;
@@ -527,12 +529,16 @@ hkv_status run_copy(bool store, const hkv_layout* layout, const void* pool,
 }
 
 // ---------------------------------------------------------------- no allocation
-// Which layout's tables the static scratch of each device holds (its serial;
-// 0 = none yet).  Calls that overlap on one device race for the scratch, as
-// the header says.
+// The directory of each device's static scratch: which layouts' tables it
+// holds, and where (hkv_scratch.hpp).  The lock and the directories are never
+// destroyed, so a layout destroyed late in process exit can still drop its
+// entries.
 constexpr int kMaxScratchDevices = 64;
-std::mutex g_scratch_mu;
-uint64_t g_scratch_holds[kMaxScratchDevices] = {};
+std::mutex& scratch_mu() {
+  static std::mutex* m = new std::mutex();
+  return *m;
+}
+hkv::ScratchDirectory* g_scratch_dir[kMaxScratchDevices] = {};
 std::atomic<uint64_t> g_next_serial{1};
 
 // The most chunks of a call whose block ids, object addresses and token
@@ -585,32 +591,45 @@ hkv_status move_noalloc(bool store, const hkv_layout* layout, void* pool,
     const int e = hkv::static_scratch(dev, &scratch);
     if (e != 0) return hip_error((hipError_t)e, "hipGetSymbolAddress (static scratch)");
   }
+  uint64_t table_off = 0;
   {
-    // The layout's tables into the scratch, unless it holds them already.
+    // The layout's tables into the scratch, unless they are there already.
     // The source is the layout's own host image; the stream is then drained
     // so that work on any other stream sees the tables whole.
-    std::lock_guard<std::mutex> g(g_scratch_mu);
-    if (g_scratch_holds[dev] != layout->serial) {
+    std::lock_guard<std::mutex> g(scratch_mu());
+    if (!g_scratch_dir[dev]) g_scratch_dir[dev] = new hkv::ScratchDirectory(hkv::kStaticScratchBytes);
+    hkv::ScratchDirectory& dir = *g_scratch_dir[dev];
+    hkv::ScratchDirectory::Entry* ent = dir.find(layout->serial);
+    if (!ent) {
       if (capturing)
-        return set_error(HKV_E_CAPTURE, "the static scratch holds another layout's tables; "
-                                        "make one call with this layout before capturing");
-      g_scratch_holds[dev] = 0;
+        return set_error(HKV_E_CAPTURE, "this layout's tables are not in the static scratch of "
+                                        "the stream's device; make one call with it there "
+                                        "before capturing");
+      int evicted = 0;
+      ent = dir.reserve(layout->serial, table_bytes, &evicted);
+      if (!ent)
+        return set_error(HKV_E_WORKSPACE, "no room in the static scratch: the layouts that "
+                                          "captured calls use fill it (destroy one first)");
       hipStream_t s = reinterpret_cast<hipStream_t>(stream);
       DeviceScope scope(dev);
-      if (scope.err != hipSuccess) return hip_error(scope.err, "selecting the stream's device");
-      hipError_t e = hipMemcpyAsync(scratch, layout->table_image.data(), table_bytes,
-                                    hipMemcpyHostToDevice, s);
-      if (e != hipSuccess) return hip_error(e, "hipMemcpyAsync (tables into the scratch)");
-      e = hipStreamSynchronize(s);
-      if (e != hipSuccess) return hip_error(e, "hipStreamSynchronize (tables into the scratch)");
-      g_scratch_holds[dev] = layout->serial;
+      hipError_t e = scope.err;
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(scratch + ent->off, layout->table_image.data(), table_bytes,
+                           hipMemcpyHostToDevice, s);
+      if (e == hipSuccess) e = hipStreamSynchronize(s);
+      if (e != hipSuccess) {
+        dir.drop(layout->serial);
+        return hip_error(e, "copying the layout's tables into the static scratch");
+      }
     }
+    dir.touch(ent, capturing);
+    table_off = ent->off;
   }
   const uint64_t n = (uint64_t)b->n_chunks;
   const uint64_t Gk = (uint64_t)p.n_kv_groups * (uint64_t)p.blocks_per_chunk;
   const uint64_t O = (uint64_t)p.n_obj_groups;
-  const uint8_t* layers = scratch;
-  const uint8_t* items = scratch + layer_table_bytes(p);
+  const uint8_t* layers = scratch + table_off;
+  const uint8_t* items = layers + layer_table_bytes(p);
   const uint32_t line_codes = codec_line_codes(p, store, b);
   uint64_t launches = 0;
   for (uint64_t c0 = 0; c0 < n; c0 += per_launch) {
@@ -642,6 +661,10 @@ hkv_layout::~hkv_layout() {
     DeviceScope scope(kv.first);
     if (scope.err == hipSuccess) (void)hipFree(kv.second);
   }
+  // its place in each device's static scratch is free again
+  std::lock_guard<std::mutex> g(scratch_mu());
+  for (hkv::ScratchDirectory* dir : g_scratch_dir)
+    if (dir) dir->drop(serial);
 }
 
 extern "C" {

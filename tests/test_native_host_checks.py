@@ -17,6 +17,7 @@ NATIVE = os.path.join(ROOT, "tests", "native")
 PROGRAMS = {
     "xcd_order.cpp": [],
     "lane_bounds.cpp": ["hkv_plan.cpp"],
+    "scratch_directory.cpp": [],
     "call_tables.cpp": ["hkv_plan.cpp", "hkv_groups.cpp"],
 }
 

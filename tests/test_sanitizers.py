@@ -29,6 +29,7 @@ ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0",
 PROGRAMS = {
     "xcd_order.cpp": [],
     "lane_bounds.cpp": ["hkv_plan.cpp"],
+    "scratch_directory.cpp": [],
     "call_tables.cpp": ["hkv_plan.cpp", "hkv_groups.cpp"],
     "api_checks.cpp": ["hkv_api.cpp", "hkv_plan.cpp", "hkv_groups.cpp", "hkv_keys.cpp"],
 }

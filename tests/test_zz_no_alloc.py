@@ -5,8 +5,8 @@ Every case runs the same calls through both entry points on twin buffers
 object byte for byte after each call: two stores in a row, the second
 smaller, then two retrieves in a row, the second smaller.  The cases cover
 calls that need several launches (more chunks than one launch's kernel
-arguments hold), null ids and partial chunks, the INT8 codec, and layouts
-that take turns on the static scratch (its tables are copied in again).
+arguments hold), null ids and partial chunks, the INT8 codec, and several
+layouts sharing the static scratch, with evictions when they outgrow it.
 The tiny workload is also checked against the oracle, full-size workloads
 run through the no-allocation entry point with every byte checked, and
 captured no-allocation calls replay correctly.
@@ -180,8 +180,8 @@ def test_noalloc_int8_codec():
 
 
 def test_noalloc_layouts_take_turns_on_the_scratch():
-    """Alternating layouts: each call whose layout's tables are not in the
-    scratch copies them in again; results stay equal."""
+    """Alternating layouts: both stay in the scratch, each at its own range;
+    results stay equal."""
     a = Twin(W.make_config("tiny").desc, 8, 0x5EED07)
     b = Twin(many_blocks_desc(), 8, 0x5EED08)
     rng = np.random.default_rng(0x5EED09)
@@ -292,15 +292,15 @@ def test_noalloc_graph_capture_replays(name):
 
 def test_noalloc_capture_refuses_a_layout_not_in_the_scratch():
     """Under capture, a no-allocation call whose layout's tables are not in
-    the static scratch (another layout's are) returns HKV_E_CAPTURE and
-    enqueues nothing: the captured graph replays only the caller's own work,
-    and the pool and objects keep their bytes."""
+    the static scratch (another layout has been used there, this one not yet)
+    returns HKV_E_CAPTURE and enqueues nothing: the captured graph replays
+    only the caller's own work, and the pool and objects keep their bytes."""
     import retrieve_store_chunk_amd as hkv
     a = Twin(W.make_config("tiny").desc, 4, 0x5EED0B)
     b = Twin(many_blocks_desc(), 4, 0x5EED0C)
     rng = np.random.default_rng(0x5EED0D)
     S = a.stream
-    # the scratch now holds b's tables
+    # the scratch now holds b's tables, not a's
     b.call("store", _ids(rng, 4, b.lay.G, b.lay.k, b.info["num_blocks"], distinct=True),
            list(range(4)))
     torch.cuda.synchronize()
@@ -317,7 +317,7 @@ def test_noalloc_capture_refuses_a_layout_not_in_the_scratch():
                                     a.pools[1].data_ptr(), ids, a.ptrs(1, range(4)),
                                     S.cuda_stream)
     assert st_store == st_retrieve == hkv.HKV_E_CAPTURE
-    assert "another layout" in hkv.hkv_last_error()
+    assert "not in the static scratch" in hkv.hkv_last_error()
     graph.replay()
     torch.cuda.synchronize()
     assert torch.equal(x.cpu(), torch.ones(16))
@@ -391,3 +391,99 @@ def test_noalloc_threads_share_one_layout():
             for o in range(ref.O):
                 assert np.array_equal(j["objs"][c][o].cpu().numpy(), objs_ref[c][o]), \
                     f"thread {t}: object {c}/{o}"
+
+
+def big_table_desc():
+    # Kimi-Linear TP=1 shapes in a pool of eight blocks: tables of about 117
+    # KB (14,317 work items per chunk), so some 35 such layouts fill the
+    # 4 MiB scratch.
+    desc = dict(W.make_config("kl_tp1").desc)
+    import retrieve_store_chunk_amd as hkv
+    stride = hkv.Layout(desc).info["block_stride"]
+    desc["pool_bytes"] = 8 * stride
+    return desc
+
+
+def _store_and_retrieve(t, rng):
+    nb = t.info["num_blocks"]
+    t.call("store", _ids(rng, 1, t.lay.G, t.lay.k, nb, distinct=True), [0])
+    t.call("retrieve", _ids(rng, 1, t.lay.G, t.lay.k, nb, distinct=True), [0])
+
+
+def test_noalloc_two_layouts_in_one_graph():
+    """Two layouts, both in the scratch after one eager call each, captured
+    together into one HIP graph.  Two replays against the same calls made
+    eagerly through the workspace entry points on the twin buffers."""
+    import retrieve_store_chunk_amd as hkv
+    a = Twin(W.make_config("tiny").desc, 4, 0x5EED30)
+    b = Twin(many_blocks_desc(), 4, 0x5EED31)
+    rng = np.random.default_rng(0x5EED32)
+    calls = []
+    for t in (a, b):
+        nb = t.info["num_blocks"]
+        t.call("store", _ids(rng, 4, t.lay.G, t.lay.k, nb, distinct=False), list(range(4)))
+        calls.append((t, "store", _ids(rng, 4, t.lay.G, t.lay.k, nb, distinct=False)))
+        calls.append((t, "retrieve", _ids(rng, 3, t.lay.G, t.lay.k, nb, distinct=True)))
+    S = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=S):
+        for t, op, ids in calls:
+            code = hkv.HKV_OP_STORE if op == "store" else hkv.HKV_OP_RETRIEVE
+            n = ids.shape[0]
+            t.lay.move_noalloc(code, t.pools[1].data_ptr(), ids, t.ptrs(1, range(n)),
+                               S.cuda_stream)
+    for rep in range(2):
+        graph.replay()
+        for t, op, ids in calls:
+            n = ids.shape[0]
+            fn = t.lay.store if op == "store" else t.lay.retrieve
+            fn(t.pools[0].data_ptr(), ids, t.ptrs(0, range(n)), t.ws.data_ptr(), t.ws_bytes,
+               t.stream.cuda_stream)
+            t.stream.synchronize()
+        torch.cuda.synchronize()
+        for t in (a, b):
+            assert torch.equal(t.pools[0], t.pools[1]), f"replay {rep}: pools differ"
+            for o in range(t.lay.O):
+                assert torch.equal(t.objs[0][o], t.objs[1][o]), f"replay {rep}: objects differ"
+
+
+def test_noalloc_evictions_keep_results_and_spare_captured_layouts():
+    """Forty layouts of about 117 KB of tables each (more than the 4 MiB
+    scratch holds), used in turn twice, so that later calls evict the least
+    recently used: every call matches the workspace entry points.  A layout
+    captured into a graph before them stays in the scratch, and its graph
+    still replays correctly afterwards."""
+    import retrieve_store_chunk_amd as hkv
+    rng = np.random.default_rng(0x5EED40)
+    pinned = Twin(W.make_config("tiny").desc, 4, 0x5EED41)
+    nb = pinned.info["num_blocks"]
+    ids_s = _ids(rng, 4, pinned.lay.G, pinned.lay.k, nb, distinct=False)
+    ids_r = _ids(rng, 3, pinned.lay.G, pinned.lay.k, nb, distinct=True)
+    pinned.call("store", ids_s, list(range(4)))
+    S = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=S):
+        pinned.lay.move_noalloc(hkv.HKV_OP_STORE, pinned.pools[1].data_ptr(), ids_s,
+                                pinned.ptrs(1, range(4)), S.cuda_stream)
+        pinned.lay.move_noalloc(hkv.HKV_OP_RETRIEVE, pinned.pools[1].data_ptr(), ids_r,
+                                pinned.ptrs(1, range(3)), S.cuda_stream)
+    desc = big_table_desc()
+    twins = [Twin(desc, 1, 0x5EED50 + i) for i in range(40)]
+    _log(f"[noalloc] eviction case: {len(twins)} layouts of {twins[0].info['num_blocks']} "
+         f"blocks each, cycled twice")
+    for cycle in range(2):
+        for t in twins:
+            _store_and_retrieve(t, rng)
+    graph.replay()
+    pinned.lay.store(pinned.pools[0].data_ptr(), ids_s, pinned.ptrs(0, range(4)),
+                     pinned.ws.data_ptr(), pinned.ws_bytes, pinned.stream.cuda_stream)
+    pinned.lay.retrieve(pinned.pools[0].data_ptr(), ids_r, pinned.ptrs(0, range(3)),
+                        pinned.ws.data_ptr(), pinned.ws_bytes, pinned.stream.cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(pinned.pools[0], pinned.pools[1]), "captured layout: pools differ"
+    for o in range(pinned.lay.O):
+        assert torch.equal(pinned.objs[0][o], pinned.objs[1][o]), "captured layout: objects"
+    del twins
+    torch.cuda.empty_cache()
