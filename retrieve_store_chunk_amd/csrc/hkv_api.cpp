@@ -621,6 +621,11 @@ hkv_status move_noalloc(bool store, const hkv_layout* layout, void* pool,
         dir.drop(layout->serial);
         return hip_error(e, "copying the layout's tables into the static scratch");
       }
+      if (trace_on())
+        std::fprintf(stderr,
+                     "[hkv] static scratch of device %d: %llu bytes of tables copied in at "
+                     "offset %llu, %d layout(s) evicted\n",
+                     dev, (unsigned long long)table_bytes, (unsigned long long)ent->off, evicted);
     }
     dir.touch(ent, capturing);
     table_off = ent->off;

@@ -487,3 +487,39 @@ def test_noalloc_evictions_keep_results_and_spare_captured_layouts():
         assert torch.equal(pinned.objs[0][o], pinned.objs[1][o]), "captured layout: objects"
     del twins
     torch.cuda.empty_cache()
+
+
+def test_noalloc_trace_reports_evictions():
+    """With HKV_TRACE=1 (a child process, so the setting is read fresh):
+    forty layouts of about 117 KB of tables, each stored through the
+    no-allocation entry point twice in turn, copy their tables in once per
+    eviction, and the copies past the array's capacity report evictions."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys, numpy as np, torch; sys.path.insert(0, %r)\n"
+        "import retrieve_store_chunk_amd as hkv\n"
+        "from tests.test_zz_no_alloc import big_table_desc\n"
+        "desc = big_table_desc()\n"
+        "lays = [hkv.Layout(desc) for _ in range(40)]\n"
+        "info = lays[0].info\n"
+        "pool = torch.zeros(info['pool_bytes_used'], dtype=torch.uint8, device='cuda')\n"
+        "objs = [torch.zeros(max(256, info['obj_bytes'][o]), dtype=torch.uint8, device='cuda')\n"
+        "        for o in range(lays[0].O)]\n"
+        "ids = np.arange(lays[0].G * lays[0].k, dtype=np.int32).reshape(1, lays[0].G, lays[0].k)\n"
+        "for cycle in range(2):\n"
+        "    for lay in lays:\n"
+        "        lay.move_noalloc(hkv.HKV_OP_STORE, pool.data_ptr(), ids,\n"
+        "                         [o.data_ptr() for o in objs])\n"
+        "torch.cuda.synchronize()\n" % root)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       env=dict(os.environ, HKV_TRACE="1"), cwd=root)
+    assert r.returncode == 0, r.stderr[-3000:]
+    copies = [ln for ln in r.stderr.splitlines() if "copied in at offset" in ln]
+    evicting = [ln for ln in copies if not ln.endswith(" 0 layout(s) evicted")]
+    # 35 fit: the first cycle copies all 40 in and evicts for the last 5; in
+    # the second, each layout's range has been taken, so it is copied in again
+    assert len(copies) == 80, (len(copies), r.stderr[-2000:])
+    assert len(evicting) >= 45, (len(evicting), copies[:3], copies[-3:])
