@@ -314,8 +314,9 @@ def build_parser() -> argparse.ArgumentParser:
                          "into several launches, timed together)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step's calls into a HIP graph after the warm-up and "
-                         "time its replays (every call's tables must fit in its kernel "
-                         "arguments; one-stream workloads only)")
+                         "time its replays (one-stream workloads only; with the workspace "
+                         "entry points every call's tables must fit in its kernel arguments, "
+                         "with --entry noalloc any call can be captured)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the reference rates timed after the steps by default: torch "
                          "copy_ of one 8 GiB buffer (the achievable device copy, also the "
