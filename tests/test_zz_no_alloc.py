@@ -224,8 +224,10 @@ def test_noalloc_oracle_round_trip_tiny():
 # Full-size workloads through the no-allocation entry point alone, in the
 # launch configuration the benchmark times: every pool byte after every wave
 # and every object byte against the bytes rebuilt from the oracle's
-# placements (the checker of the full-size parity tests).
-NOALLOC_FULL_SIZE = ["kl_tp1", "k3_tp8_holes", "long_ctx", "kl_tp1_int8", "kl_tp1_int8_host"]
+# placements (the checker of the full-size parity tests).  Every workload but
+# the duplex one, whose retrieves go by DMA (the entry point runs kernels).
+NOALLOC_FULL_SIZE = [n for n in W.CONFIG_NAMES + W.EXTRA_CONFIG_NAMES
+                     if W.make_config(n).extra.get("retrieve_engine", "kernel") == "kernel"]
 
 
 @pytest.mark.parametrize("name", NOALLOC_FULL_SIZE)
